@@ -1,0 +1,277 @@
+"""Seeded synthetic inputs for the MoE token-reordering path.
+
+This module only draws random inputs; it holds none of the operations'
+arithmetic.  Both the CPU oracle's tests and the HIP path's tests / benchmark
+take their inputs from here, so the two sides always see identical bytes.
+
+Element storage follows the oracle's convention: FP16 as ``numpy.float16``,
+BF16 as ``numpy.uint16`` bit patterns (the top 16 bits of a float32 draw),
+FP32 as ``numpy.float32``, INT8 as ``numpy.int8``.
+
+Named workloads (the shapes and value distributions of the five standard
+cases):
+
+=====  ===========================================================================
+case   recipe
+=====  ===========================================================================
+1      batching: A=2, BS=8, K+1=3 (Y=48), H=128 FP16 ~N(0,1); 16 experts, 1 layer;
+       expert ids uniform [0,16); 5 slots masked
+2      batching: A=16, BS=32, K+1=9 (Y=4608), H=7168 BF16 ~N(0,1); 256 experts;
+       ids = perm[r], r ~ p(r) proportional to (r+1)^-1.1 (Zipf s=1.1), perm a
+       random permutation of the experts; 230 slots masked (5%)
+3      batching: A=64, BS=64, K+1=9 (Y=36864), H=7168 INT8 uniform [-127,127] with
+       a packed FP32 scale ~U(1e-3,1e-1) per row (row stride H+4); 16 layers x
+       64 experts (expertNum=1024); layer of chunk a = a mod 16; ids uniform
+       [0,64); 7373 slots masked (20%)
+4      unpermute, non-padded, FP32 probs: T=16384, topK=8, E=128, H=4096 BF16
+       ~N(0,1) permuted rows [T*topK, H]; 13107 slots (10%) = -1; the valid slots
+       read permuted rows given by a random permutation of [0, #valid); token t's
+       routing-map row has (#valid slots of t) ones at random experts; probs =
+       softmax of N(0,1) logits over those experts, 0 elsewhere
+5      unpermute, padded, FP16 probs: E=64, capacity C=512 (rows = 32768),
+       H=5120 FP16 ~N(0,1), T=8192; each expert's C sortedIndices entries are
+       drawn from [0,T) without replacement; routing map = top-4 of N(0,1)
+       logits per token; probs = FP16 softmax over the top-4, 0 elsewhere
+=====  ===========================================================================
+
+All masks and -1 sets are exact counts drawn without replacement, so byte
+counts of a case are deterministic.
+"""
+
+import os
+
+import numpy as np
+
+FP16, BF16, INT8, FP32 = 0, 1, 2, 3
+_ELT = {FP16: 2, BF16: 2, INT8: 1, FP32: 4}
+
+
+_CHUNK = 1 << 22   # elements per independently seeded block of a large draw
+
+
+def _convert_block(x, dt):
+    if dt == FP16:
+        return x.astype(np.float16)
+    if dt == BF16:
+        return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    if dt == FP32:
+        return x
+    raise ValueError(dt)
+
+
+def _normal_elements(rng, shape, dt):
+    """N(0,1) elements of type ``dt``.
+
+    Large draws are split into blocks of ``_CHUNK`` elements, each with its own
+    child generator spawned from ``rng``, and filled on a thread pool; the
+    result depends only on the seed and the shape, not on the thread count.
+    """
+    n = int(np.prod(shape))
+    if n <= _CHUNK:
+        return _convert_block(rng.standard_normal(size=shape, dtype=np.float32), dt)
+    out_dtype = {FP16: np.float16, BF16: np.uint16, FP32: np.float32}[dt]
+    out = np.empty(n, dtype=out_dtype)
+    nblk = (n + _CHUNK - 1) // _CHUNK
+    children = rng.spawn(nblk)
+
+    def fill(b):
+        lo, hi = b * _CHUNK, min(n, (b + 1) * _CHUNK)
+        out[lo:hi] = _convert_block(children[b].standard_normal(size=hi - lo, dtype=np.float32), dt)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
+
+
+def _softmax_rows(logits, keep):
+    """Row softmax over the kept entries; rows with nothing kept are all zero."""
+    any_kept = keep.any(axis=1, keepdims=True)
+    z = np.where(keep, logits.astype(np.float64), -1e300)
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.where(keep, np.exp(z), 0.0)
+    s = np.where(any_kept, e.sum(axis=1, keepdims=True), 1.0)
+    return e / s
+
+
+# ----------------------------------------------------------------------------- batching
+
+def batching_case(seed, A, BS, K1, H, expert_num, layer_num, token_dtype,
+                  n_masked=0, expert_dist="uniform", zipf_s=1.1, layer_of_chunk=None,
+                  n_bad_ids=0, with_id_tables=False, stride_pad=0, separate_scale=False):
+    """Draw one batching input.
+
+    Returns a dict: ``token_bytes`` uint8 [Y, stride] (row s = slot s; for INT8
+    with ``separate_scale`` False the FP32 scale sits in bytes [H, H+4)),
+    ``token_scale`` float32 [Y] or None, ``expert_ids`` int32 [Y], ``mask``
+    uint8 [Y] or None, ``layer_ids`` / ``session_ids`` / ``micro_batch_ids``
+    int32 [A] or None, plus the scalar parameters.
+    """
+    rng = np.random.default_rng(seed)
+    Y = A * BS * K1
+    L = max(layer_num, 1)
+    per_layer = expert_num // L
+    elt = _ELT[token_dtype]
+    row = H * elt
+    if token_dtype == INT8:
+        data = rng.integers(-127, 128, size=(Y, H), dtype=np.int16).astype(np.int8)
+        scale = rng.uniform(1e-3, 1e-1, size=Y).astype(np.float32)
+        payload = data.view(np.uint8).reshape(Y, H)
+        if separate_scale:
+            stride = row + stride_pad
+            tb = np.zeros((Y, stride), dtype=np.uint8)
+            tb[:, :row] = payload
+            token_scale = scale
+        else:
+            stride = row + 4 + stride_pad
+            tb = np.zeros((Y, stride), dtype=np.uint8)
+            tb[:, :row] = payload
+            tb[:, row:row + 4] = scale.view(np.uint8).reshape(Y, 4)
+            token_scale = None
+    else:
+        data = _normal_elements(rng, (Y, H), token_dtype)
+        stride = row + stride_pad
+        tb = np.zeros((Y, stride), dtype=np.uint8)
+        tb[:, :row] = data.view(np.uint8).reshape(Y, row)
+        token_scale = None
+
+    if expert_dist == "uniform":
+        ids = rng.integers(0, per_layer, size=Y).astype(np.int32)
+    elif expert_dist == "zipf":
+        p = (np.arange(per_layer, dtype=np.float64) + 1.0) ** (-zipf_s)
+        p /= p.sum()
+        r = rng.choice(per_layer, size=Y, p=p)
+        perm = rng.permutation(per_layer)
+        ids = perm[r].astype(np.int32)
+    elif expert_dist == "modulo":
+        ids = (np.arange(Y) % (BS * K1) % per_layer).astype(np.int32)
+    else:
+        raise ValueError(expert_dist)
+
+    mask = None
+    if n_masked:
+        mask = np.zeros(Y, dtype=np.uint8)
+        mask[rng.choice(Y, size=n_masked, replace=False)] = 1
+    if n_bad_ids:
+        bad = rng.choice(Y, size=n_bad_ids, replace=False)
+        vals = rng.choice(np.array([-1, -7, per_layer, per_layer + 3, 1 << 30]), size=n_bad_ids)
+        ids[bad] = vals.astype(np.int32)
+
+    layer_ids = None
+    if layer_num >= 1 and (layer_of_chunk is not None or L > 1):
+        if layer_of_chunk == "mod":
+            layer_ids = (np.arange(A) % L).astype(np.int32)
+        else:
+            layer_ids = rng.integers(0, L, size=A).astype(np.int32)
+    session_ids = micro_batch_ids = None
+    if with_id_tables:
+        session_ids = rng.integers(0, 1 << 20, size=A).astype(np.int32)
+        micro_batch_ids = rng.integers(0, 64, size=A).astype(np.int32)
+
+    return dict(token_bytes=tb, token_scale=token_scale, expert_ids=ids, mask=mask,
+                layer_ids=layer_ids, session_ids=session_ids, micro_batch_ids=micro_batch_ids,
+                A=A, BS=BS, K1=K1, H=H, expert_num=expert_num, layer_num=layer_num,
+                token_dtype=token_dtype, stride=stride)
+
+
+def batching_config(n):
+    """The named batching workloads 1-3 (see the module table)."""
+    if n == 1:
+        return batching_case(1, A=2, BS=8, K1=3, H=128, expert_num=16, layer_num=1,
+                             token_dtype=FP16, n_masked=5)
+    if n == 2:
+        return batching_case(2, A=16, BS=32, K1=9, H=7168, expert_num=256, layer_num=1,
+                             token_dtype=BF16, n_masked=230, expert_dist="zipf")
+    if n == 3:
+        return batching_case(3, A=64, BS=64, K1=9, H=7168, expert_num=1024, layer_num=16,
+                             token_dtype=INT8, n_masked=7373, layer_of_chunk="mod")
+    raise ValueError(n)
+
+
+# ----------------------------------------------------------------------------- unpermute
+
+def unpermute_nonpadded_case(seed, T, K, E, H, dtype, probs_dtype=None, n_empty=0,
+                             with_probs=True, rows_mode="compact"):
+    """Non-padded (token-slot) input: sortedIndices [T*K], permuted rows [T*K, H].
+
+    ``rows_mode`` "compact": the valid slots read a random permutation of rows
+    [0, #valid); "slots": they read a random permutation of their own slot
+    indices.
+    """
+    rng = np.random.default_rng(seed)
+    N = T * K
+    x = _normal_elements(rng, (N, H), dtype)
+    sI = np.full(N, -1, dtype=np.int32)
+    empty = np.zeros(N, dtype=bool)
+    if n_empty:
+        empty[rng.choice(N, size=n_empty, replace=False)] = True
+    valid_slots = np.nonzero(~empty)[0]
+    if rows_mode == "compact":
+        sI[valid_slots] = rng.permutation(valid_slots.shape[0]).astype(np.int32)
+    else:
+        sI[valid_slots] = rng.permutation(valid_slots).astype(np.int32)
+    routing_map = probs = None
+    if with_probs:
+        n_t = (~empty).reshape(T, K).sum(axis=1)
+        routing_map = np.zeros((T, E), dtype=np.int8)
+        for t in range(T):
+            if n_t[t]:
+                routing_map[t, rng.choice(E, size=int(n_t[t]), replace=False)] = 1
+        logits = rng.standard_normal(size=(T, E))
+        p = _softmax_rows(logits, routing_map != 0)
+        probs = _probs_storage(p, probs_dtype)
+    return dict(permuted=x, dtype=dtype, sorted_indices=sI, routing_map=routing_map,
+                probs=probs, probs_dtype=probs_dtype if with_probs else None,
+                padded_mode=False, restore_shape=(T, H), T=T, K=K, E=E, H=H)
+
+
+def unpermute_padded_case(seed, E, C, T, H, dtype, probs_dtype=None, topk=4,
+                          with_probs=True, n_invalid=0):
+    """Padded (expert-capacity) input: sortedIndices [E*C] of token ids."""
+    rng = np.random.default_rng(seed)
+    N = E * C
+    x = _normal_elements(rng, (N, H), dtype)
+    sI = np.empty(N, dtype=np.int32)
+    for e in range(E):
+        sI[e * C:(e + 1) * C] = rng.choice(T, size=C, replace=C > T)
+    if n_invalid:
+        pos = rng.choice(N, size=n_invalid, replace=False)
+        sI[pos] = rng.choice(np.array([-1, T, T + 5, -3]), size=n_invalid).astype(np.int32)
+    routing_map = probs = None
+    if with_probs:
+        logits = rng.standard_normal(size=(T, E))
+        k = min(topk, E)
+        top = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        routing_map = np.zeros((T, E), dtype=np.int8)
+        np.put_along_axis(routing_map, top, 1, axis=1)
+        p = _softmax_rows(logits, routing_map != 0)
+        probs = _probs_storage(p, probs_dtype)
+    return dict(permuted=x, dtype=dtype, sorted_indices=sI, routing_map=routing_map,
+                probs=probs, probs_dtype=probs_dtype if with_probs else None,
+                padded_mode=True, restore_shape=(T, H), T=T, E=E, C=C, H=H)
+
+
+def _probs_storage(p, dt):
+    p32 = p.astype(np.float32)
+    if dt == FP32:
+        return p32
+    if dt == FP16:
+        return p32.astype(np.float16)
+    if dt == BF16:
+        return (p32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(dt)
+
+
+def unpermute_config(n):
+    """The named unpermute workloads 4 and 5 (see the module table)."""
+    if n == 4:
+        return unpermute_nonpadded_case(4, T=16384, K=8, E=128, H=4096, dtype=BF16,
+                                        probs_dtype=FP32, n_empty=13107)
+    if n == 5:
+        return unpermute_padded_case(5, E=64, C=512, T=8192, H=5120, dtype=FP16,
+                                     probs_dtype=FP16, topk=4)
+    raise ValueError(n)
+
+
+def config(n):
+    return batching_config(n) if n <= 3 else unpermute_config(n)
