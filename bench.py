@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE token-reordering hot path on one MI355X.
+
+One step = one pass of the whole path over the four large synthetic workloads, each a
+single library call on the current stream:
+  batching BF16   A=16 BS=32 K+1=9  H=7168, 256 experts (Zipf 1.1), 5% masked
+  batching INT8   A=64 BS=64 K+1=9  H=7168 + FP32 scale, 16 layers x 64 experts, 20% masked
+  unpermute non-padded  T=16384 topK=8 E=128 H=4096 BF16, FP32 probs, 10% empty slots
+  unpermute padded      E=64 C=512 T=8192 H=5120 FP16, FP16 probs (top-4)
+The printed value is effective HBM bandwidth: the step's algorithmic bytes (every input
+byte the operations need, read once, plus every output byte, written once) divided by
+the measured step time.  Inputs are resident in HBM before timing; the step's working
+set (~2 GB) is far above the 256 MB Infinity Cache, so steps do not hit in it.
+
+Also reported: per-workload times with the caches flushed between iterations, the
+roofline of the dominant kernel (the non-padded gather-reduce, timed with HIP events
+on its own stream position), and the CPU oracle timed on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (and % of peak) for batching and unpermute; rows/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "unpermute_reduce_nonpadded_bf16_T16384_topk8_H4096.traffic.txt")
+REDUCE_SOURCES = ["unpermute_ffnwb_batching_amd/csrc/unpermute.hip",
+                  "unpermute_ffnwb_batching_amd/csrc/device_common.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--detail-iters", type=int, default=20, help="per-workload timed iterations (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of workloads to keep (profiling runs)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- algorithmic bytes
+
+def batching_bytes(c, actual):
+    Y = c["A"] * c["BS"] * c["K1"]
+    row = c["H"] * (1 if c["token_dtype"] == 2 else 2)
+    b = 4 * Y + (Y if c["mask"] is not None else 0) + (4 * c["A"] if c["layer_ids"] is not None else 0)
+    b += actual * (2 * row + 16 + (8 if c["token_dtype"] == 2 else 0))
+    b += 16 * c["expert_num"] + 8
+    return b
+
+
+def nonpadded_bytes(c):
+    T, H = c["restore_shape"]
+    sI = c["sorted_indices"]
+    N = sI.size
+    elt = 4 if c["dtype"] == 3 else 2
+    pelt = 4 if c["probs_dtype"] == 3 else 2
+    valid = int(((sI >= 0) & (sI < N)).sum())
+    nnz = int((c["routing_map"] != 0).sum())
+    E = c["routing_map"].shape[1]
+    return T * E + nnz * pelt + 4 * N + valid * H * elt + T * H * elt + N * pelt + 8 * N
+
+
+def nonpadded_reduce_bytes(c):
+    """Bytes the gather-reduce kernel alone must move: indices, valid rows and their
+    weights, and the output rows."""
+    T, H = c["restore_shape"]
+    sI = c["sorted_indices"]
+    N = sI.size
+    elt = 4 if c["dtype"] == 3 else 2
+    pelt = 4 if c["probs_dtype"] == 3 else 2
+    valid = int(((sI >= 0) & (sI < N)).sum())
+    return 4 * N + valid * (H * elt + pelt) + T * H * elt
+
+
+def padded_bytes(c):
+    T, H = c["restore_shape"]
+    sI = c["sorted_indices"]
+    N = sI.size
+    elt = 4 if c["dtype"] == 3 else 2
+    pelt = 4 if c["probs_dtype"] == 3 else 2
+    nval = int(((sI >= 0) & (sI < T)).sum())
+    return 4 * N + nval * pelt + nval * H * elt + T * H * elt + N * pelt + 8 * N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in REDUCE_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(per_launch_alg):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary,
+    or None when the summary is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build targets one GPU; --gpus {args.gpus} is not supported "
+              "(every workload is one GPU's share; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import unpermute_ffnwb_batching_amd as F
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _gpu import (prepare_batching, prepare_unpermute, fetch_batching, fetch_unpermute,
+                      check_batching, check_unpermute)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    names = ["batching_bf16", "batching_int8", "unpermute_nonpadded", "unpermute_padded"]
+    if args.only:
+        names = [n for n in names if n in args.only.split(",")]
+    cases = {}
+    for n in names:
+        cases[n] = {"batching_bf16": lambda: synth.batching_config(2),
+                    "batching_int8": lambda: synth.batching_config(3),
+                    "unpermute_nonpadded": lambda: synth.unpermute_config(4),
+                    "unpermute_padded": lambda: synth.unpermute_config(5)}[n]()
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    calls = {}
+    for n, c in cases.items():
+        calls[n] = prepare_batching(c) if n.startswith("batching") else prepare_unpermute(c)
+    torch.cuda.synchronize()
+
+    # algorithmic bytes and rows per workload (actual_token_num from the first run)
+    for call in calls.values():
+        call.run()
+    torch.cuda.synchronize()
+    alg, rows = {}, {}
+    for n, c in cases.items():
+        if n.startswith("batching"):
+            act = int(calls[n].out["actual_token_num"].item())
+            alg[n], rows[n] = batching_bytes(c, act), act
+        elif n == "unpermute_nonpadded":
+            alg[n] = nonpadded_bytes(c)
+            sI = c["sorted_indices"]
+            rows[n] = int(((sI >= 0) & (sI < sI.size)).sum())
+        else:
+            alg[n] = padded_bytes(c)
+            rows[n] = int(((c["sorted_indices"] >= 0) & (c["sorted_indices"] < c["restore_shape"][0])).sum())
+    step_bytes = sum(alg.values())
+
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    have_np = "unpermute_nonpadded" in calls
+    hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(i=None):
+        for n, call in calls.items():
+            if n == "unpermute_nonpadded":
+                if i is None:
+                    call.set_reduce_events(None, None)
+                else:
+                    call.set_reduce_events(*hot[i])
+            call.run(stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    hot_ms = float(np.mean([b.elapsed_time(e) for b, e in hot])) if have_np else None
+    print(f"# {K} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # per-workload timing with L2 / Infinity Cache flushed before every iteration
+    detail = {}
+    if args.detail_iters > 0:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        for n, call in calls.items():
+            ts = []
+            for _ in range(args.detail_iters):
+                flush.fill_(1)
+                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                call.run(stream)
+                e.record(stream)
+                e.synchronize()
+                ts.append(b.elapsed_time(e))
+            med = float(np.median(ts))
+            detail[n] = {"us_median": round(med * 1e3, 2), "us_p10": round(float(np.percentile(ts, 10)) * 1e3, 2),
+                         "us_p90": round(float(np.percentile(ts, 90)) * 1e3, 2),
+                         "alg_bytes": alg[n], "GBps": round(alg[n] / med / 1e6, 1),
+                         "pct_hbm_peak": round(100 * alg[n] / med / 1e6 / HBM_PEAK_GBS, 1),
+                         "rows_per_s": round(rows[n] / med * 1e3, 1)}
+        del flush
+
+    # parity of the timed outputs and the CPU oracle baseline, on the host
+    parity = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        from _gpu import oracle_batching, oracle_unpermute
+        t_or = {}
+        refs = {}
+        for n, c in cases.items():
+            t1 = time.perf_counter()
+            refs[n] = oracle_batching(c) if n.startswith("batching") else oracle_unpermute(c)
+            t_or[n] = time.perf_counter() - t1
+        secs = sum(t_or.values())
+        cpu = {"value": round(step_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "one full step (all four workloads) through the NumPy oracle, single-threaded; "
+                         f"{secs:.1f} s on {os.cpu_count()} visible host cores",
+               "seconds_per_workload": {n: round(v, 3) for n, v in t_or.items()}}
+        parity = True
+        for n, c in cases.items():
+            try:
+                if n.startswith("batching"):
+                    check_batching(c, fetch_batching(calls[n]), refs[n])
+                else:
+                    check_unpermute(c, fetch_unpermute(calls[n], c), refs[n])
+            except AssertionError as ex:
+                parity = False
+                print(f"# parity FAILED for {n}: {ex}", file=sys.stderr, flush=True)
+
+    roof = None
+    if have_np:
+        red_bytes = nonpadded_reduce_bytes(cases["unpermute_nonpadded"])
+        achieved = red_bytes / (hot_ms * 1e-3) / 1e9
+        traffic = read_traffic(red_bytes)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "unpermute_reduce_kernel (non-padded, BF16 rows, FP32 weights)",
+                "alg_bytes_per_launch": red_bytes, "avg_launch_us": round(hot_ms * 1e3, 2)}
+
+    value = step_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "moe_reorder_suite: " + "+".join(names),
+                   "step_alg_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "element_types": "bf16/int8 rows moved; fp32 accumulation in unpermute"},
+        "roofline": roof, "cpu_baseline": cpu, "configs": detail, "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * ffnwb.h -- C ABI of the MI355X (gfx950) MoE token-reordering library.
+ *
+ * Two operations, each with the two-phase shape of the pages' aclnn interface
+ * (a host-only workspace query that also validates every argument, then an
+ * asynchronous launch on a caller stream):
+ *
+ *   ffnwb_batching  -- FFN-worker batching.  Defined by the aclnnFfnWorkerBatching
+ *                      API page ("Function description" steps 2-4, the
+ *                      calculation formula, the parameter and output tables,
+ *                      "Constraints").
+ *   moe_unpermute   -- MoE token unpermute with routing map.  Defined by the
+ *                      article "MoeTokenUnpermuteWithRoutingMap 算子全解析",
+ *                      section "Function description and formulas" (four
+ *                      branches: padded x has-probs), "Parameters",
+ *                      "Supplementary notes", "Constraints", "Return values
+ *                      and error codes".
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; it only enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the legacy default stream) and returns.
+ *   - The caller allocates the workspace (device memory of the size the query
+ *     returned, 256-byte aligned) and keeps it alive until the work on `stream`
+ *     has finished.  Its contents on entry do not matter.
+ *   - Inputs are read-only.  Inputs and outputs must not overlap.
+ *   - Calls are stateless and may run concurrently on different streams with
+ *     distinct workspaces and outputs.
+ *   - Every result is deterministic (bit-identical across runs).
+ *   - Data errors inside arrays never fault: out-of-range ids / indices are
+ *     treated as masked (batching) or skipped (unpermute), as documented below.
+ *
+ * Status codes: FFNWB_OK, or one of the values below.  Validation happens in
+ * full before anything is enqueued, so an error return leaves every output
+ * untouched.
+ */
+#ifndef FFNWB_H
+#define FFNWB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFNWB_ABI_VERSION 1
+
+/* Status codes.  The first three take the aclnn values both pages list. */
+#define FFNWB_OK                 0
+#define FFNWB_ERR_PARAM_NULLPTR  161001 /* a required pointer is NULL */
+#define FFNWB_ERR_PARAM_INVALID  161002 /* a type, shape or range is outside the supported set */
+#define FFNWB_ERR_INNER_NULLPTR  561103 /* unpermute: topK > 512, or probs has an unsupported shape */
+#define FFNWB_ERR_WORKSPACE      1      /* workspace NULL or smaller than the query returned */
+#define FFNWB_ERR_RUNTIME        2      /* the HIP runtime refused a launch or a device query */
+
+/* Element types. 0..2 are the batching page's tokenDtype values. */
+#define FFNWB_DT_FP16 0
+#define FFNWB_DT_BF16 1
+#define FFNWB_DT_INT8 2 /* batching only: INT8 data with an FP32 dynamic scale per row */
+#define FFNWB_DT_FP32 3 /* unpermute only */
+
+/* ------------------------------------------------------------------------------------------
+ * FFN-worker batching (aclnnFfnWorkerBatching API page).
+ *
+ * Y = A * BS * K1 slots; slot s belongs to chunk a = s / (BS*K1) (one
+ * (session, micro-batch) block of the attention->FFN data area).  Slot s is
+ * valid when it is not masked, its expert id lies in [0, expert_num/L) and its
+ * chunk's layer id lies in [0, L), L = max(layer_num, 1).  Its sort key is
+ * layer * (expert_num / L) + expert_id.  Valid slots are emitted in ascending
+ * key order, ties in ascending slot order (stable), as output rows
+ * i = 0 .. actual_token_num-1:
+ *   y[i]               = token row of slot g_i (H elements, bit copy)
+ *   token_ids[i]       = g_i
+ *   expert_offsets[i]  = i - (first output row of g_i's key)
+ *   session_ids_out[i] = session_ids[a] (or a when session_ids is NULL)
+ *   micro_batch_ids_out[i] = micro_batch_ids[a] (or 0 when NULL)
+ *   dynamic_scale[i]   = scale of slot g_i (INT8 only)
+ * Rows i >= actual_token_num of the per-row outputs are NOT written.
+ * group_list[j] = {key_j, count_j} for the j-th present key in ascending order,
+ * then {0, 0} rows up to expert_num rows; actual_token_num = sum of counts.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct ffnwb_batching_desc {
+  /* maxOutShape {A, BS, topK+1, H}: A in (0,1024], BS > 0, K1 in (0,64], H > 0. */
+  int64_t A, BS, K1, H;
+  int64_t expert_num;    /* experts on this device over all layers, in (0, 8192] */
+  int64_t layer_num;     /* in [0, expert_num]; 0 behaves as 1; expert_num % max(layer_num,1) == 0 */
+  int32_t token_dtype;   /* FFNWB_DT_FP16, FFNWB_DT_BF16 or FFNWB_DT_INT8 */
+  int32_t need_schedule; /* must be 0: the caller supplies mask / layer_ids itself */
+
+  /* Inputs. */
+  const void* token_data;    /* Y rows; row s starts at token_data + s*token_row_stride (bytes) */
+  int64_t token_row_stride;  /* bytes; 0 = H*elt, or H+4 for INT8 with a packed scale */
+  const float* token_scale;  /* INT8: NULL = scale packed at byte H of each token row
+                                (the page's contiguous layout); else scale of slot s at
+                                (char*)token_scale + s*scale_stride */
+  int64_t scale_stride;      /* bytes; 0 = 4 for a separate array */
+  const int32_t* expert_ids; /* [Y] expert id of each slot, indexed within its layer */
+  const uint8_t* mask;       /* [Y] non-zero = slot masked; NULL = no slot masked */
+  const int32_t* layer_ids;  /* [A] layer of each chunk; NULL = layer 0 */
+  const int32_t* session_ids;     /* [A] or NULL */
+  const int32_t* micro_batch_ids; /* [A] or NULL */
+
+  /* Outputs (all required except err_count; dynamic_scale required for INT8 only). */
+  void* y;                       /* [Y, H] dense, element type token_dtype */
+  int32_t* session_ids_out;      /* [Y] */
+  int32_t* micro_batch_ids_out;  /* [Y] */
+  int32_t* token_ids;            /* [Y] */
+  int32_t* expert_offsets;       /* [Y] */
+  float* dynamic_scale;          /* [Y] */
+  int64_t* group_list;           /* [expert_num, 2] */
+  int64_t* actual_token_num;     /* [1] */
+  int32_t* err_count;            /* [1] or NULL: number of unmasked slots whose expert or layer
+                                    id was out of range (such slots are dropped) */
+
+  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
+     the row-gather kernel.  NULL = not recorded. */
+  void* ev_gather_begin;
+  void* ev_gather_end;
+} ffnwb_batching_desc;
+
+/* Validates *d and returns the workspace size in bytes (host only, no device work).
+   Errors: FFNWB_ERR_PARAM_NULLPTR (d, ws_bytes or a required array NULL),
+   FFNWB_ERR_PARAM_INVALID (a range above violated). */
+int ffnwb_batching_workspace_size(const ffnwb_batching_desc* d, size_t* ws_bytes);
+
+/* Validates again, then enqueues the batching on `stream`.  `workspace` must hold at
+   least the queried size (FFNWB_ERR_WORKSPACE otherwise; NULL allowed when it is 0). */
+int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * MoE token unpermute with routing map (MoeTokenUnpermuteWithRoutingMap article).
+ *
+ * T = num_tokens, H = hidden, N = num_indices, E = num_experts.
+ * Non-padded mode (padded_mode = 0): topK = N / T; slot i = t*topK + k reads permuted
+ *   row r = sorted_indices[i]; slots with r outside [0, num_rows) (e.g. -1) are skipped.
+ *     out[t] = RNE( sum_k  f32(x[r]) * w )        (FP32 products and sums, k ascending)
+ *   with w = permute_probs[r] (weight_index 0) or permute_probs[i] (weight_index 1),
+ *   w = 1 without probs.  permute_probs = probs^T compacted under routing_map^T
+ *   (expert-major order of the (token, expert) pairs with a non-zero map entry),
+ *   zero-padded to N.  out_index = stable argsort of the slots by sorted_indices,
+ *   invalid slots first; permute_token_id = out_index / topK.
+ * Padded mode (padded_mode = 1): capacity C = N / E.  permute_token_id / out_index =
+ *   stable sort of sorted_indices (values / source positions); entries outside [0, T)
+ *   sort after all valid ones and are not accumulated.  permute_probs[i] =
+ *   probs[sorted_indices[i], i / C] (0 for invalid entries).
+ *     out[t] = RNE( sum_{j : permute_token_id[j] == t, j ascending} f32(x[out_index[j]]) * w )
+ *   with w = permute_probs[out_index[j]], or 1 without probs.
+ * Every element of out is written (+0.0 where nothing accumulates).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct moe_unpermute_desc {
+  int32_t dtype;        /* permuted / unpermuted tokens: FFNWB_DT_FP16, _BF16 or _FP32 */
+  int32_t probs_dtype;  /* = dtype, or FFNWB_DT_FP32 when dtype is BF16; ignored without probs */
+  int32_t padded_mode;  /* 0 = token-slot layout, 1 = expert-capacity layout */
+  int32_t weight_index; /* non-padded with probs: 0 = weight of the permuted row (default),
+                           1 = weight of the slot */
+  int64_t num_rows;     /* rows of permuted_tokens; must equal num_indices */
+  int64_t hidden;       /* H > 0 */
+  int64_t num_tokens;   /* T = restoreShape[0] (= probs rows when probs are given), >= 0 */
+  int64_t num_experts;  /* E = probs columns, in (0, 8192]; 0 without probs */
+  int64_t num_indices;  /* N = length of sorted_indices */
+
+  /* Inputs. */
+  const void* permuted_tokens;   /* [num_rows, H] */
+  const int32_t* sorted_indices; /* [N] */
+  const uint8_t* routing_map;    /* [T, E] INT8 {0,1} or BOOL, or NULL; NULL iff probs NULL */
+  const void* probs;             /* [T, E] of probs_dtype, or NULL */
+
+  /* Outputs. unpermuted_tokens is required; the other three may be NULL to skip them. */
+  void* unpermuted_tokens;  /* [T, H] of dtype */
+  int32_t* out_index;       /* [N] */
+  int32_t* permute_token_id;/* [N] */
+  void* permute_probs;      /* [N] of probs_dtype (only with probs) */
+
+  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
+     the gather-reduce kernel.  NULL = not recorded. */
+  void* ev_reduce_begin;
+  void* ev_reduce_end;
+} moe_unpermute_desc;
+
+/* Validates *d and returns the workspace size in bytes (host only, no device work).
+   Errors: FFNWB_ERR_PARAM_NULLPTR (required pointer NULL), FFNWB_ERR_PARAM_INVALID
+   (dtype combination, routing_map/probs NULL mismatch, num_rows != N, N not a multiple
+   of T (non-padded) or of E (padded with probs), sizes out of range),
+   FFNWB_ERR_INNER_NULLPTR (topK > 512, or num_experts outside (0, 8192] with probs). */
+int moe_unpermute_workspace_size(const moe_unpermute_desc* d, size_t* ws_bytes);
+
+/* Validates again, then enqueues the unpermute on `stream`. */
+int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ffnwb_status_string(int status);
+
+/* FFNWB_ABI_VERSION of the built library. */
+int ffnwb_abi_version(void);
+
+/* sizeof the two descriptors as compiled into the library (binding self-check). */
+size_t ffnwb_batching_desc_size(void);
+size_t moe_unpermute_desc_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFNWB_H */

@@ -1,0 +1,180 @@
+"""Helpers for the GPU parity tests: move a seeded case to the device, run the HIP
+library through its binding, bring the outputs back in the oracle's storage format,
+and compare with the oracle."""
+
+import numpy as np
+import torch
+
+import synth
+import unpermute_ffnwb_batching_amd as F
+
+# The oracle is imported only by the functions that compare with it, so that the
+# benchmark can use the device-side helpers below without loading the oracle outside
+# its CPU-baseline leg.
+
+CANARY = 0xA5
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _canary(shape, dtype):
+    nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    return torch.full((nbytes,), CANARY, dtype=torch.uint8, device="cuda").view(dtype).reshape(shape)
+
+
+def _bytes(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+_TOKEN_TORCH = {0: torch.float16, 1: torch.bfloat16, 2: torch.int8}
+
+
+# ----------------------------------------------------------------------------- batching
+
+def oracle_batching(case):
+    from oracle import ffn_worker_batching
+    return ffn_worker_batching(
+        case["token_bytes"], case["expert_ids"], case["expert_num"], case["layer_num"],
+        (case["A"], case["BS"], case["K1"], case["H"]), case["token_dtype"],
+        mask=case["mask"], layer_ids=case["layer_ids"], session_ids=case["session_ids"],
+        micro_batch_ids=case["micro_batch_ids"], token_scale=case["token_scale"])
+
+
+def prepare_batching(case, ev_gather=None):
+    A, BS, K1, H = case["A"], case["BS"], case["K1"], case["H"]
+    Y = A * BS * K1
+    td = case["token_dtype"]
+    out = {"y": _canary((Y, H), _TOKEN_TORCH[td]),
+           "group_list": _canary((case["expert_num"], 2), torch.int64),
+           "actual_token_num": _canary((1,), torch.int64),
+           "err_count": _canary((1,), torch.int32)}
+    for k in ("session_ids", "micro_batch_ids", "token_ids", "expert_offsets"):
+        out[k] = _canary((Y,), torch.int32)
+    if td == 2:
+        out["dynamic_scale"] = _canary((Y,), torch.float32)
+    opt = {k: (dev(case[k]) if case[k] is not None else None)
+           for k in ("mask", "layer_ids", "session_ids", "micro_batch_ids", "token_scale")}
+    return F.BatchingCall(dev(case["token_bytes"]), dev(case["expert_ids"]), expert_num=case["expert_num"],
+                          layer_num=case["layer_num"], max_out_shape=(A, BS, K1, H), token_dtype=td,
+                          token_row_stride=case["stride"], out=out, ev_gather=ev_gather, **opt)
+
+
+def fetch_batching(call):
+    o = call.out
+    r = {"y": _bytes(o["y"]).reshape(o["y"].shape[0], -1)}
+    for k, v in o.items():
+        if k != "y":
+            r[k] = v.cpu().numpy()
+    return r
+
+
+def run_batching(case):
+    call = prepare_batching(case)
+    call.run()
+    torch.cuda.synchronize()
+    return fetch_batching(call)
+
+
+def check_batching(case, got, ref=None):
+    ref = ref if ref is not None else oracle_batching(case)
+    act = ref["actual_token_num"]
+    Y = case["A"] * case["BS"] * case["K1"]
+    assert int(got["actual_token_num"][0]) == act
+    assert np.array_equal(got["group_list"], ref["group_list"])
+    assert int(got["err_count"][0]) == ref["err_count"]
+    assert np.array_equal(got["y"][:act], ref["y"]), "gathered rows differ"
+    for k in ("token_ids", "expert_offsets", "session_ids", "micro_batch_ids"):
+        assert np.array_equal(got[k][:act], ref[k]), k
+    if case["token_dtype"] == 2:
+        assert np.array_equal(got["dynamic_scale"][:act].view(np.uint32), ref["dynamic_scale"].view(np.uint32))
+    # rows past actual_token_num are never written
+    assert (got["y"][act:] == CANARY).all()
+    canary32 = np.uint32(0xA5A5A5A5).view(np.int32)
+    for k in ("token_ids", "expert_offsets", "session_ids", "micro_batch_ids"):
+        assert (got[k][act:Y] == canary32).all(), k
+    return ref
+
+
+# ----------------------------------------------------------------------------- unpermute
+
+def to_torch_elems(a, dt):
+    if dt == synth.BF16:
+        return dev(np.asarray(a).view(np.int16)).view(torch.bfloat16)
+    return dev(a)
+
+
+def from_torch_elems(t, dt):
+    a = t.cpu()
+    if dt == synth.BF16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    return a.numpy()
+
+
+def oracle_unpermute(case, weight_index=0):
+    from oracle import moe_token_unpermute_with_routing_map
+    return moe_token_unpermute_with_routing_map(
+        case["permuted"], case["dtype"], case["sorted_indices"], case["padded_mode"], case["restore_shape"],
+        routing_map=case["routing_map"], probs=case["probs"], probs_dtype=case["probs_dtype"],
+        weight_index=weight_index)
+
+
+def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None):
+    T, H = case["restore_shape"]
+    N = case["sorted_indices"].shape[0]
+    x = to_torch_elems(case["permuted"], case["dtype"])
+    probs = to_torch_elems(case["probs"], case["probs_dtype"]) if case["probs"] is not None else None
+    rmap = dev(case["routing_map"]) if case["routing_map"] is not None else None
+    out = {"unpermuted": _canary((T, H), x.dtype)}
+    if aux:
+        out["out_index"] = _canary((N,), torch.int32)
+        out["permute_token_id"] = _canary((N,), torch.int32)
+    if probs is not None:
+        out["permute_probs"] = _canary((N,), probs.dtype)
+    return F.UnpermuteCall(x, dev(case["sorted_indices"]), rmap, probs, padded_mode=case["padded_mode"],
+                           restore_shape=(T, H), weight_index=weight_index, aux=aux, out=out, ev_reduce=ev_reduce)
+
+
+def fetch_unpermute(call, case):
+    o = call.out
+    r = {"unpermuted": from_torch_elems(o["unpermuted"], case["dtype"])}
+    for k in ("out_index", "permute_token_id"):
+        if k in o:
+            r[k] = o[k].cpu().numpy()
+    if "permute_probs" in o:
+        r["permute_probs"] = from_torch_elems(o["permute_probs"], case["probs_dtype"])
+    return r
+
+
+def run_unpermute(case, weight_index=0, aux=True):
+    call = prepare_unpermute(case, weight_index, aux)
+    call.run()
+    torch.cuda.synchronize()
+    return fetch_unpermute(call, case)
+
+
+TOL = {synth.FP16: (1e-2, 1e-3), synth.BF16: (1e-2, 1e-3), synth.FP32: (1e-5, 1e-6)}
+
+
+def check_unpermute(case, got, ref=None, weight_index=0, aux=True, bit_exact=True):
+    from oracle import numerics as nm
+    ref = ref if ref is not None else oracle_unpermute(case, weight_index)
+    dt = case["dtype"]
+    g = nm.to_f32(got["unpermuted"], dt)
+    o = nm.to_f32(ref["unpermuted"], dt)
+    rtol, atol = TOL[dt]
+    # acceptance bar: bf16/fp16 within 1e-2 relative or 1e-3 absolute; fp32 within 1e-5 relative
+    np.testing.assert_allclose(g, o, rtol=rtol, atol=atol)
+    if bit_exact:
+        # same FP32 operations in the same order as the oracle: identical bits
+        gb = np.asarray(got["unpermuted"]).view(np.uint8)
+        ob = np.asarray(ref["unpermuted"]).view(np.uint8)
+        assert np.array_equal(gb, ob), "unpermuted differs in bits from the oracle"
+    if aux:
+        assert np.array_equal(got["out_index"], ref["out_index"])
+        assert np.array_equal(got["permute_token_id"], ref["permute_token_id"])
+    if case["probs"] is not None:
+        assert np.array_equal(np.asarray(got["permute_probs"]).view(np.uint8),
+                              np.asarray(ref["permute_probs"]).view(np.uint8))
+    return ref

@@ -1,0 +1,193 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/ffnwb.h declares, its descriptor layout matches the binding, and
+argument validation returns the documented status codes before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import unpermute_ffnwb_batching_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # a non-NULL address; the workspace queries never dereference pointers
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ffnwb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", src, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for n in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
+              "moe_unpermute", "ffnwb_status_string", "ffnwb_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_descriptor_layout_and_version():
+    L = F.lib()
+    assert L.ffnwb_batching_desc_size() == ctypes.sizeof(F.BatchingDesc)
+    assert L.moe_unpermute_desc_size() == ctypes.sizeof(F.UnpermuteDesc)
+    assert F.ffnwb_abi_version() == 1
+    for st in (0, 161001, 161002, 561103, 1, 2):
+        assert F.ffnwb_status_string(st).startswith("FFNWB_")
+
+
+# ----------------------------------------------------------------------------- batching
+
+def _batching_desc(**over):
+    d = F.BatchingDesc()
+    vals = dict(A=2, BS=8, K1=3, H=128, expert_num=16, layer_num=1, token_dtype=0, need_schedule=0)
+    vals.update({k: v for k, v in over.items() if k in vals})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    for p in ("token_data", "expert_ids", "y", "session_ids_out", "micro_batch_ids_out", "token_ids",
+              "expert_offsets", "dynamic_scale", "group_list", "actual_token_num"):
+        setattr(d, p, FAKE)
+    for k, v in over.items():
+        if k not in vals:
+            setattr(d, k, v)
+    return d
+
+
+def _bws(d):
+    n = ctypes.c_size_t(0)
+    st = F.lib().ffnwb_batching_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_batching_valid_and_small_path_needs_no_workspace():
+    st, n = _bws(_batching_desc())
+    assert st == 0 and n == 0                       # Y = 48 runs in one fused workgroup
+
+
+@pytest.mark.parametrize("field", ["token_data", "expert_ids", "y", "session_ids_out", "micro_batch_ids_out",
+                                   "token_ids", "expert_offsets", "group_list", "actual_token_num"])
+def test_batching_required_pointers(field):
+    assert _bws(_batching_desc(**{field: None}))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+
+
+def test_batching_int8_requires_dynamic_scale():
+    assert _bws(_batching_desc(token_dtype=2, dynamic_scale=None))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+    assert _bws(_batching_desc(token_dtype=0, dynamic_scale=None))[0] == 0
+
+
+@pytest.mark.parametrize("over", [
+    dict(expert_num=0), dict(expert_num=8193), dict(A=0), dict(A=1025), dict(BS=0), dict(K1=0), dict(K1=65),
+    dict(H=0), dict(token_dtype=3), dict(token_dtype=-1), dict(need_schedule=1), dict(need_schedule=2),
+    dict(layer_num=-1), dict(layer_num=17), dict(expert_num=16, layer_num=3),
+    dict(token_row_stride=255), dict(token_dtype=2, token_row_stride=130),
+])
+def test_batching_invalid_parameters(over):
+    assert _bws(_batching_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_batching_boundaries_accepted():
+    for over in (dict(expert_num=8192), dict(A=1024), dict(K1=64), dict(layer_num=0), dict(layer_num=16),
+                 dict(token_dtype=2, token_row_stride=132), dict(token_dtype=1)):
+        assert _bws(_batching_desc(**over))[0] == 0, over
+
+
+def test_batching_workspace_grows_with_slots():
+    sizes = [_bws(_batching_desc(A=a, BS=64, K1=9, H=7168, expert_num=1024, layer_num=16))[1]
+             for a in (4, 16, 64, 256)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+
+
+def test_batching_launch_rejects_small_workspace_before_any_device_work():
+    d = _batching_desc(A=64, BS=64, K1=9, H=7168, expert_num=1024, layer_num=16)
+    st, n = _bws(d)
+    assert st == 0 and n > 0
+    assert F.lib().ffnwb_batching(ctypes.byref(d), None, ctypes.c_size_t(n), None) == F.FFNWB_ERR_WORKSPACE
+    assert F.lib().ffnwb_batching(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_size_t(n - 1),
+                                  None) == F.FFNWB_ERR_WORKSPACE
+    bad = _batching_desc(expert_num=0)
+    assert F.lib().ffnwb_batching(ctypes.byref(bad), None, 0, None) == F.FFNWB_ERR_PARAM_INVALID
+
+
+# ----------------------------------------------------------------------------- unpermute
+
+def _unpermute_desc(probs=True, **over):
+    d = F.UnpermuteDesc()
+    vals = dict(dtype=1, probs_dtype=3, padded_mode=0, weight_index=0, num_rows=64, hidden=32,
+                num_tokens=8, num_experts=4 if probs else 0, num_indices=64)
+    vals.update({k: v for k, v in over.items() if k in vals})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    for p in ("permuted_tokens", "sorted_indices", "unpermuted_tokens", "out_index", "permute_token_id"):
+        setattr(d, p, FAKE)
+    if probs:
+        d.routing_map = FAKE
+        d.probs = FAKE
+        d.permute_probs = FAKE
+    for k, v in over.items():
+        if k not in vals:
+            setattr(d, k, v)
+    return d
+
+
+def _uws(d):
+    n = ctypes.c_size_t(0)
+    st = F.lib().moe_unpermute_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_unpermute_valid_cases():
+    assert _uws(_unpermute_desc())[0] == 0
+    assert _uws(_unpermute_desc(probs=False))[0] == 0
+    assert _uws(_unpermute_desc(padded_mode=1, num_experts=4))[0] == 0
+    assert _uws(_unpermute_desc(num_tokens=0, num_rows=0, num_indices=0))[0] == 0     # empty
+    assert _uws(_unpermute_desc(dtype=1, probs_dtype=1))[0] == 0
+    assert _uws(_unpermute_desc(dtype=0, probs_dtype=0))[0] == 0
+    assert _uws(_unpermute_desc(dtype=3, probs_dtype=3))[0] == 0
+    assert _uws(_unpermute_desc(num_tokens=1, num_rows=512, num_indices=512))[0] == 0  # topK = 512
+
+
+@pytest.mark.parametrize("field", ["permuted_tokens", "sorted_indices", "unpermuted_tokens"])
+def test_unpermute_required_pointers(field):
+    assert _uws(_unpermute_desc(**{field: None}))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+
+
+def test_unpermute_optional_outputs_may_be_null():
+    assert _uws(_unpermute_desc(out_index=None, permute_token_id=None, permute_probs=None))[0] == 0
+
+
+@pytest.mark.parametrize("over", [
+    dict(dtype=2), dict(dtype=7), dict(dtype=0, probs_dtype=3), dict(dtype=3, probs_dtype=1),
+    dict(dtype=1, probs_dtype=0), dict(routing_map=None), dict(padded_mode=2), dict(weight_index=2),
+    dict(hidden=0), dict(num_rows=63), dict(num_indices=65, num_rows=65), dict(num_tokens=-1),
+    dict(num_tokens=0), dict(padded_mode=1, num_experts=5),
+])
+def test_unpermute_invalid_parameters(over):
+    assert _uws(_unpermute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_unpermute_probs_without_map_is_invalid():
+    d = _unpermute_desc(probs=False)
+    d.probs = FAKE
+    d.probs_dtype = 3
+    assert _uws(d)[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+@pytest.mark.parametrize("over", [
+    dict(num_tokens=1, num_rows=513, num_indices=513),     # topK = 513 > 512
+    dict(num_experts=0), dict(num_experts=8193),
+])
+def test_unpermute_inner_nullptr_code(over):
+    assert _uws(_unpermute_desc(**over))[0] == F.FFNWB_ERR_INNER_NULLPTR
+
+
+def test_unpermute_workspace_skips_aux_sort_when_not_requested():
+    full = _uws(_unpermute_desc(num_tokens=16384, num_rows=131072, num_indices=131072, num_experts=128))[1]
+    lean = _uws(_unpermute_desc(num_tokens=16384, num_rows=131072, num_indices=131072, num_experts=128,
+                                out_index=None, permute_token_id=None))[1]
+    assert lean < full

@@ -1,0 +1,114 @@
+"""GPU parity of moe_unpermute against the oracle: the acceptance tolerance and, since
+the kernels use the oracle's FP32 operation order without fused multiply-adds, identical
+bits; index and prob outputs are bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import check_unpermute, prepare_unpermute, fetch_unpermute, run_unpermute, oracle_unpermute
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_named_cases_full_size(n):
+    case = synth.unpermute_config(n)
+    print(f"unpermute case {n}", flush=True)
+    check_unpermute(case, run_unpermute(case))
+
+
+NONPAD = [
+    # (T, K, E, H, dtype, probs dtype, n_empty, with_probs, rows_mode)
+    (1, 1, 1, 8, synth.FP32, synth.FP32, 0, True, "compact"),
+    (7, 3, 5, 24, synth.FP16, synth.FP16, 4, True, "slots"),
+    (64, 8, 16, 4096, synth.BF16, synth.FP32, 50, True, "compact"),
+    (40, 4, 9, 136, synth.BF16, synth.BF16, 0, True, "slots"),
+    (33, 5, 12, 19, synth.FP16, synth.FP16, 30, True, "compact"),     # odd H: element path
+    (50, 6, 1, 64, synth.FP32, None, 60, False, "slots"),              # branch 4, no probs
+    (3000, 8, 64, 32, synth.BF16, synth.FP32, 2000, True, "compact"),  # aux order needs 2 LSD passes
+    (2, 512, 600, 16, synth.FP16, synth.FP16, 100, True, "slots"),    # topK = 512
+    (1000, 2, 300, 264, synth.FP32, synth.FP32, 0, True, "compact"),
+]
+
+
+@pytest.mark.parametrize("params", NONPAD, ids=[str(i) for i in range(len(NONPAD))])
+def test_nonpadded_random(params):
+    T, K, E, H, dt, pdt, empty, wp, mode = params
+    case = synth.unpermute_nonpadded_case(500 + T + K, T=T, K=K, E=E, H=H, dtype=dt, probs_dtype=pdt,
+                                          n_empty=empty, with_probs=wp, rows_mode=mode)
+    print(f"unpermute nonpadded {params}", flush=True)
+    check_unpermute(case, run_unpermute(case))
+
+
+PAD = [
+    # (E, C, T, H, dtype, probs dtype, topk, with_probs, n_invalid)
+    (1, 1, 1, 8, synth.FP32, synth.FP32, 1, True, 0),
+    (2, 1, 2, 2, synth.FP32, synth.FP32, 2, True, 0),
+    (8, 40, 100, 264, synth.FP16, synth.FP16, 3, True, 5),
+    (16, 64, 50, 128, synth.BF16, synth.FP32, 2, True, 0),     # capacity > tokens (with replacement)
+    (4, 33, 200, 21, synth.BF16, synth.BF16, 1, True, 7),     # odd H
+    (6, 10, 30, 64, synth.FP16, None, 0, False, 3),           # branch 3, no probs
+    (4, 8, 25000, 32, synth.FP32, synth.FP32, 2, True, 2),    # token count needs LSD passes
+]
+
+
+@pytest.mark.parametrize("params", PAD, ids=[str(i) for i in range(len(PAD))])
+def test_padded_random(params):
+    E, C, T, H, dt, pdt, topk, wp, inv = params
+    case = synth.unpermute_padded_case(900 + E + C, E=E, C=C, T=T, H=H, dtype=dt, probs_dtype=pdt, topk=topk,
+                                       with_probs=wp, n_invalid=inv)
+    print(f"unpermute padded {params}", flush=True)
+    check_unpermute(case, run_unpermute(case))
+
+
+def test_article_padded_example():
+    case = dict(permuted=np.ones((2, 2), np.float32), dtype=synth.FP32,
+                sorted_indices=np.array([1, 1], np.int32), routing_map=np.ones((2, 2), np.int8),
+                probs=np.ones((2, 2), np.float32), probs_dtype=synth.FP32, padded_mode=True,
+                restore_shape=(2, 2))
+    got = run_unpermute(case)
+    check_unpermute(case, got)
+    assert got["unpermuted"].tolist() == [[0.0, 0.0], [2.0, 2.0]]
+
+
+def test_weight_index_slot_reading():
+    case = synth.unpermute_nonpadded_case(31, T=200, K=4, E=32, H=256, dtype=synth.BF16,
+                                          probs_dtype=synth.FP32, n_empty=90)
+    check_unpermute(case, run_unpermute(case, weight_index=1), oracle_unpermute(case, 1), weight_index=1)
+
+
+def test_aux_outputs_skipped():
+    case = synth.unpermute_nonpadded_case(32, T=128, K=8, E=64, H=512, dtype=synth.FP16,
+                                          probs_dtype=synth.FP16, n_empty=100)
+    check_unpermute(case, run_unpermute(case, aux=False), aux=False)
+    pcase = synth.unpermute_padded_case(33, E=8, C=64, T=300, H=256, dtype=synth.FP16, probs_dtype=synth.FP16)
+    check_unpermute(pcase, run_unpermute(pcase, aux=False), aux=False)
+
+
+def test_empty_inputs():
+    # no slots at all for some tokens, and no entries at all
+    case = synth.unpermute_nonpadded_case(34, T=16, K=2, E=4, H=64, dtype=synth.FP16, probs_dtype=synth.FP16,
+                                          n_empty=32)
+    check_unpermute(case, run_unpermute(case))
+    empty = dict(permuted=np.zeros((0, 64), np.float16), dtype=synth.FP16, sorted_indices=np.zeros(0, np.int32),
+                 routing_map=None, probs=None, probs_dtype=None, padded_mode=True, restore_shape=(5, 64))
+    got = run_unpermute(empty)
+    assert (got["unpermuted"].view(np.uint16) == 0).all()
+    nz = dict(empty, padded_mode=False, restore_shape=(0, 64))
+    run_unpermute(nz)
+
+
+def test_deterministic_repeat():
+    case = synth.unpermute_padded_case(35, E=16, C=128, T=1000, H=512, dtype=synth.BF16, probs_dtype=synth.FP32)
+    call = prepare_unpermute(case)
+    call.run()
+    torch.cuda.synchronize()
+    a = fetch_unpermute(call, case)
+    call.run()
+    torch.cuda.synchronize()
+    b = fetch_unpermute(call, case)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+    check_unpermute(case, b)

@@ -1,0 +1,289 @@
+"""Python binding of libffnwb (include/ffnwb.h): MoE token reordering on MI355X.
+
+Argument marshalling only -- every step of both operations runs in the library's HIP
+kernels.  PyTorch provides device memory and the current HIP stream.
+
+The names mirror the C ABI:
+
+* ``ffnwb_batching_workspace_size`` / ``ffnwb_batching``
+* ``moe_unpermute_workspace_size`` / ``moe_unpermute``
+* ``ffnwb_status_string``, ``ffnwb_abi_version``
+
+``ffnwb_batching`` and ``moe_unpermute`` take torch tensors, allocate any output or
+workspace the caller did not pass, fill the C descriptor and enqueue the call on the
+current stream.  ``BatchingCall`` / ``UnpermuteCall`` build the descriptor once for
+repeated launches (benchmarks, graph capture).
+
+The library must be built (``python -m unpermute_ffnwb_batching_amd.build``); importing
+works without it, but every call then raises ``RuntimeError``: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to (same soname)
+
+from . import _abi
+from ._abi import (FFNWB_OK, FFNWB_ERR_PARAM_NULLPTR, FFNWB_ERR_PARAM_INVALID,  # noqa: F401
+                   FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME,
+                   FFNWB_DT_FP16, FFNWB_DT_BF16, FFNWB_DT_INT8, FFNWB_DT_FP32,
+                   BatchingDesc, UnpermuteDesc)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libffnwb.so")
+_lib = None
+
+
+class FfnwbError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: status {status} ({ffnwb_status_string(status)})")
+        self.status = status
+
+
+def lib():
+    """The loaded shared library (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run python -m unpermute_ffnwb_batching_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.ffnwb_batching_workspace_size.argtypes = [ctypes.POINTER(BatchingDesc), ctypes.POINTER(sz)]
+        L.ffnwb_batching.argtypes = [ctypes.POINTER(BatchingDesc), vp, sz, vp]
+        L.moe_unpermute_workspace_size.argtypes = [ctypes.POINTER(UnpermuteDesc), ctypes.POINTER(sz)]
+        L.moe_unpermute.argtypes = [ctypes.POINTER(UnpermuteDesc), vp, sz, vp]
+        for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
+                  "moe_unpermute", "ffnwb_abi_version"):
+            getattr(L, f).restype = ctypes.c_int
+        L.ffnwb_status_string.argtypes = [ctypes.c_int]
+        L.ffnwb_status_string.restype = ctypes.c_char_p
+        L.ffnwb_batching_desc_size.restype = sz
+        L.moe_unpermute_desc_size.restype = sz
+        if L.ffnwb_batching_desc_size() != ctypes.sizeof(BatchingDesc) or \
+                L.moe_unpermute_desc_size() != ctypes.sizeof(UnpermuteDesc):
+            raise RuntimeError("libffnwb descriptor layout does not match the Python binding")
+        if L.ffnwb_abi_version() != _abi.FFNWB_ABI_VERSION:
+            raise RuntimeError("libffnwb ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def ffnwb_status_string(status):
+    return lib().ffnwb_status_string(int(status)).decode()
+
+
+def ffnwb_abi_version():
+    return lib().ffnwb_abi_version()
+
+
+_placeholders = {}
+
+
+def _ptr(t):
+    """Device address of a tensor; an empty tensor gets a valid placeholder address
+    (the library never reads it: every size that would index it is 0)."""
+    if t is None:
+        return None
+    if t.numel() == 0:
+        key = str(t.device)
+        if key not in _placeholders:
+            _placeholders[key] = torch.empty(256, dtype=torch.uint8, device=t.device)
+        return ctypes.c_void_p(_placeholders[key].data_ptr())
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------- batching
+
+_TOKEN_TORCH = {FFNWB_DT_FP16: torch.float16, FFNWB_DT_BF16: torch.bfloat16, FFNWB_DT_INT8: torch.int8}
+_ELT = {FFNWB_DT_FP16: 2, FFNWB_DT_BF16: 2, FFNWB_DT_INT8: 1, FFNWB_DT_FP32: 4}
+
+
+def ffnwb_batching_workspace_size(desc):
+    n = ctypes.c_size_t(0)
+    st = lib().ffnwb_batching_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != FFNWB_OK:
+        raise FfnwbError(st, "ffnwb_batching_workspace_size")
+    return n.value
+
+
+def _row_stride_bytes(t):
+    return t.stride(0) * t.element_size() if t.dim() >= 2 else 0
+
+
+class BatchingCall:
+    """A prepared ffnwb_batching call: descriptor, outputs and workspace bound once.
+
+    ``token_data`` is a device tensor whose dim-0 rows are the Y slots (any element
+    type; its row stride in bytes is passed as token_row_stride).  Outputs are
+    allocated unless given in ``out`` (a dict with any of the keys below).
+    """
+
+    OUT_KEYS = ("y", "group_list", "actual_token_num", "session_ids", "micro_batch_ids",
+                "token_ids", "expert_offsets", "dynamic_scale", "err_count")
+
+    def __init__(self, token_data, expert_ids, *, expert_num, layer_num, max_out_shape, token_dtype,
+                 mask=None, layer_ids=None, session_ids=None, micro_batch_ids=None, token_scale=None,
+                 token_row_stride=None, scale_stride=0, need_schedule=0, out=None, with_err_count=True,
+                 workspace=None, ev_gather=None):
+        A, BS, K1, H = (int(v) for v in max_out_shape)
+        Y = A * BS * K1
+        dev = token_data.device
+        out = dict(out or {})
+        i32 = dict(dtype=torch.int32, device=dev)
+        tdt = _TOKEN_TORCH.get(int(token_dtype), torch.uint8)
+        if "y" not in out:
+            out["y"] = torch.empty((Y, H), dtype=tdt, device=dev)
+        if "group_list" not in out:
+            out["group_list"] = torch.empty((int(expert_num), 2), dtype=torch.int64, device=dev)
+        if "actual_token_num" not in out:
+            out["actual_token_num"] = torch.empty(1, dtype=torch.int64, device=dev)
+        for k in ("session_ids", "micro_batch_ids", "token_ids", "expert_offsets"):
+            if k not in out:
+                out[k] = torch.empty(Y, **i32)
+        if int(token_dtype) == FFNWB_DT_INT8 and "dynamic_scale" not in out:
+            out["dynamic_scale"] = torch.empty(Y, dtype=torch.float32, device=dev)
+        if with_err_count and "err_count" not in out:
+            out["err_count"] = torch.empty(1, **i32)
+        self.out = out
+        self._keep = [token_data, expert_ids, mask, layer_ids, session_ids, micro_batch_ids, token_scale]
+
+        d = BatchingDesc()
+        d.A, d.BS, d.K1, d.H = A, BS, K1, H
+        d.expert_num = int(expert_num)
+        d.layer_num = int(layer_num)
+        d.token_dtype = int(token_dtype)
+        d.need_schedule = int(need_schedule)
+        d.token_data = _ptr(token_data)
+        d.token_row_stride = _row_stride_bytes(token_data) if token_row_stride is None else int(token_row_stride)
+        d.token_scale = _ptr(token_scale)
+        d.scale_stride = int(scale_stride)
+        d.expert_ids = _ptr(expert_ids)
+        d.mask = _ptr(mask)
+        d.layer_ids = _ptr(layer_ids)
+        d.session_ids = _ptr(session_ids)
+        d.micro_batch_ids = _ptr(micro_batch_ids)
+        d.y = _ptr(out["y"])
+        d.session_ids_out = _ptr(out["session_ids"])
+        d.micro_batch_ids_out = _ptr(out["micro_batch_ids"])
+        d.token_ids = _ptr(out["token_ids"])
+        d.expert_offsets = _ptr(out["expert_offsets"])
+        d.dynamic_scale = _ptr(out.get("dynamic_scale"))
+        d.group_list = _ptr(out["group_list"])
+        d.actual_token_num = _ptr(out["actual_token_num"])
+        d.err_count = _ptr(out.get("err_count"))
+        if ev_gather is not None:
+            d.ev_gather_begin = ctypes.c_void_p(ev_gather[0].cuda_event)
+            d.ev_gather_end = ctypes.c_void_p(ev_gather[1].cuda_event)
+        self.desc = d
+        self.ws_bytes = ffnwb_batching_workspace_size(d)
+        if workspace is None and self.ws_bytes:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+
+    def set_gather_events(self, begin, end):
+        self.desc.ev_gather_begin = None if begin is None else ctypes.c_void_p(begin.cuda_event)
+        self.desc.ev_gather_end = None if end is None else ctypes.c_void_p(end.cuda_event)
+
+    def run(self, stream=None):
+        ws = self.workspace
+        st = lib().ffnwb_batching(ctypes.byref(self.desc), _ptr(ws), ctypes.c_size_t(self.ws_bytes),
+                                  _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "ffnwb_batching")
+        return self.out
+
+
+def ffnwb_batching(token_data, expert_ids, *, stream=None, **kw):
+    """Run FFN-worker batching once; returns the dict of output tensors."""
+    return BatchingCall(token_data, expert_ids, **kw).run(stream)
+
+
+# ----------------------------------------------------------------------------- unpermute
+
+_FLOAT_CODE = {torch.float16: FFNWB_DT_FP16, torch.bfloat16: FFNWB_DT_BF16, torch.float32: FFNWB_DT_FP32}
+
+
+def moe_unpermute_workspace_size(desc):
+    n = ctypes.c_size_t(0)
+    st = lib().moe_unpermute_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != FFNWB_OK:
+        raise FfnwbError(st, "moe_unpermute_workspace_size")
+    return n.value
+
+
+class UnpermuteCall:
+    """A prepared moe_unpermute call.
+
+    ``permuted_tokens`` [rows, H] (fp16 / bf16 / fp32), ``sorted_indices`` int32 [N],
+    ``routing_map`` int8/bool [T, E] or None, ``probs`` [T, E] or None.
+    ``aux`` False skips out_index / permute_token_id.
+    """
+
+    def __init__(self, permuted_tokens, sorted_indices, routing_map=None, probs=None, *, padded_mode,
+                 restore_shape, weight_index=0, aux=True, out=None, workspace=None, ev_reduce=None):
+        T, H = (int(v) for v in restore_shape)
+        dev = permuted_tokens.device
+        out = dict(out or {})
+        N = sorted_indices.numel()
+        if "unpermuted" not in out:
+            out["unpermuted"] = torch.empty((T, H), dtype=permuted_tokens.dtype, device=dev)
+        if aux:
+            for k in ("out_index", "permute_token_id"):
+                if k not in out:
+                    out[k] = torch.empty(N, dtype=torch.int32, device=dev)
+        if probs is not None and "permute_probs" not in out:
+            out["permute_probs"] = torch.empty(N, dtype=probs.dtype, device=dev)
+        self.out = out
+        rm = routing_map
+        if rm is not None and rm.dtype == torch.bool:
+            rm = rm.view(torch.uint8)
+        self._keep = [permuted_tokens, sorted_indices, rm, probs]
+
+        d = UnpermuteDesc()
+        d.dtype = _FLOAT_CODE.get(permuted_tokens.dtype, -1)
+        d.probs_dtype = _FLOAT_CODE.get(probs.dtype, -1) if probs is not None else 0
+        d.padded_mode = int(bool(padded_mode))
+        d.weight_index = int(weight_index)
+        d.num_rows = permuted_tokens.shape[0]
+        d.hidden = H if permuted_tokens.dim() < 2 else permuted_tokens.shape[1]
+        d.num_tokens = T
+        d.num_experts = probs.shape[1] if probs is not None else 0
+        d.num_indices = N
+        d.permuted_tokens = _ptr(permuted_tokens)
+        d.sorted_indices = _ptr(sorted_indices)
+        d.routing_map = _ptr(rm)
+        d.probs = _ptr(probs)
+        d.unpermuted_tokens = _ptr(out["unpermuted"])
+        d.out_index = _ptr(out.get("out_index"))
+        d.permute_token_id = _ptr(out.get("permute_token_id"))
+        d.permute_probs = _ptr(out.get("permute_probs"))
+        if ev_reduce is not None:
+            d.ev_reduce_begin = ctypes.c_void_p(ev_reduce[0].cuda_event)
+            d.ev_reduce_end = ctypes.c_void_p(ev_reduce[1].cuda_event)
+        self.desc = d
+        self.ws_bytes = moe_unpermute_workspace_size(d)
+        if workspace is None and self.ws_bytes:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+
+    def set_reduce_events(self, begin, end):
+        self.desc.ev_reduce_begin = None if begin is None else ctypes.c_void_p(begin.cuda_event)
+        self.desc.ev_reduce_end = None if end is None else ctypes.c_void_p(end.cuda_event)
+
+    def run(self, stream=None):
+        st = lib().moe_unpermute(ctypes.byref(self.desc), _ptr(self.workspace), ctypes.c_size_t(self.ws_bytes),
+                                 _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "moe_unpermute")
+        return self.out
+
+
+def moe_unpermute(permuted_tokens, sorted_indices, routing_map=None, probs=None, *, stream=None, **kw):
+    """Run the unpermute once; returns dict(unpermuted, out_index, permute_token_id, permute_probs)."""
+    return UnpermuteCall(permuted_tokens, sorted_indices, routing_map, probs, **kw).run(stream)

@@ -1,0 +1,85 @@
+// C ABI entry points: validation, workspace sizing and dispatch (include/ffnwb.h).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "internal.hpp"
+
+namespace ffnwb {
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("FFNWB_LOG");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  return on;
+}
+
+void log_warn(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  fprintf(stderr, "[ffnwb] warning: ");
+  vfprintf(stderr, fmt, ap);
+  fprintf(stderr, "\n");
+  va_end(ap);
+}
+
+}  // namespace ffnwb
+
+using namespace ffnwb;
+
+extern "C" {
+
+int ffnwb_abi_version(void) { return FFNWB_ABI_VERSION; }
+
+size_t ffnwb_batching_desc_size(void) { return sizeof(ffnwb_batching_desc); }
+
+size_t moe_unpermute_desc_size(void) { return sizeof(moe_unpermute_desc); }
+
+const char* ffnwb_status_string(int status) {
+  switch (status) {
+    case FFNWB_OK: return "FFNWB_OK";
+    case FFNWB_ERR_PARAM_NULLPTR: return "FFNWB_ERR_PARAM_NULLPTR: a required pointer is NULL";
+    case FFNWB_ERR_PARAM_INVALID: return "FFNWB_ERR_PARAM_INVALID: a type, shape or range is not supported";
+    case FFNWB_ERR_INNER_NULLPTR: return "FFNWB_ERR_INNER_NULLPTR: topK > 512 or unsupported probs shape";
+    case FFNWB_ERR_WORKSPACE: return "FFNWB_ERR_WORKSPACE: workspace missing or smaller than required";
+    case FFNWB_ERR_RUNTIME: return "FFNWB_ERR_RUNTIME: the HIP runtime rejected a launch";
+    default: return "unknown ffnwb status";
+  }
+}
+
+int ffnwb_batching_workspace_size(const ffnwb_batching_desc* d, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  BatchingPlan p;
+  const int st = plan_batching(d, &p);
+  if (st != FFNWB_OK) return st;
+  *ws_bytes = p.ws_bytes;
+  return FFNWB_OK;
+}
+
+int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  BatchingPlan p;
+  const int st = plan_batching(d, &p);
+  if (st != FFNWB_OK) return st;
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  return launch_batching(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_unpermute_workspace_size(const moe_unpermute_desc* d, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  UnpermutePlan p;
+  const int st = plan_unpermute(d, &p);
+  if (st != FFNWB_OK) return st;
+  *ws_bytes = p.ws_bytes;
+  return FFNWB_OK;
+}
+
+int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  UnpermutePlan p;
+  const int st = plan_unpermute(d, &p);
+  if (st != FFNWB_OK) return st;
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  return launch_unpermute(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,401 @@
+// FFN-worker batching on gfx950 (aclnnFfnWorkerBatching API page, "Function description"
+// steps 2-4 and the calculation formula).
+//
+// Three launches in the general case:
+//   1. sort_rank_kernel<KeyBatching>: per slot key (masked / bad ids -> not placed), stable
+//      in-tile rank, per-tile key histogram (bucket-major), per-tile count of bad ids;
+//   2. scan_hist_kernel: exclusive scan of the histogram -> first output row of every
+//      (key, tile) run; its tail writes group_list, actual_token_num and err_count;
+//   3. batching_gather_kernel: one wavefront per slot copies the slot's H-element row to
+//      its output row with 16-byte accesses and writes the per-row IDs and scale.
+// Small problems (one tile, small rows) run all three steps in one workgroup.
+#include <stdio.h>
+
+#include "internal.hpp"
+#include "sort_engine.hpp"
+
+namespace ffnwb {
+
+struct BatchArgs {
+  int64_t Y, chunk;
+  int32_t per_layer, L, layer_num;
+  const int32_t* expert_ids;
+  const uint8_t* mask;
+  const int32_t* layer_ids;
+  const int32_t* session_ids;
+  const int32_t* micro_batch_ids;
+  const uint8_t* token_data;
+  int64_t stride;
+  const uint8_t* scale_base;  // INT8 only
+  int64_t scale_stride;
+  uint8_t* y;
+  int64_t row_bytes;
+  int32_t* session_out;
+  int32_t* mb_out;
+  int32_t* token_ids;
+  int32_t* offsets;
+  float* dyn_scale;           // nullptr unless INT8
+};
+
+// Slot key: layer * experts_per_layer + expert id; masked slots do not take part, and
+// unmasked slots with an out-of-range expert or layer id are dropped and counted.
+struct KeyBatching {
+  BatchArgs a;
+  __device__ uint32_t key(int64_t s, bool& valid, bool& err) const {
+    valid = false; err = false;
+    if (a.mask != nullptr && a.mask[s] != 0) return 0;
+    const int64_t c = s / a.chunk;
+    const int32_t layer = (a.layer_ids != nullptr && a.layer_num >= 1) ? a.layer_ids[c] : 0;
+    const int32_t e = a.expert_ids[s];
+    if (e < 0 || e >= a.per_layer || layer < 0 || layer >= a.L) { err = true; return 0; }
+    valid = true;
+    return static_cast<uint32_t>(layer * a.per_layer + e);
+  }
+};
+
+// Copies one row with the calling wavefront.  VEC = 16: every address 16-byte aligned;
+// VEC = 4: 4-byte aligned (16-byte accesses at dword alignment, dword tail); VEC = 1: bytes.
+template <int VEC>
+__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t bytes,
+                                         uint32_t lane) {
+  constexpr int U = 8;
+  if (VEC == 1) {
+    for (int64_t i = lane; i < bytes; i += kWave) dst[i] = src[i];
+    return;
+  }
+  typedef typename std::conditional<VEC == 16, u32x4, u32x4_a4>::type V;
+  const V* s4 = reinterpret_cast<const V*>(src);
+  V* d4 = reinterpret_cast<V*>(dst);
+  const int64_t n16 = bytes >> 4;
+  for (int64_t b = 0; b < n16; b += kWave * U) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) v[u] = s4[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) d4[i] = v[u];
+    }
+  }
+  if (VEC == 4) {
+    const int64_t tail = (bytes & 15) >> 2;
+    if (lane < tail) {
+      reinterpret_cast<uint32_t*>(dst + n16 * 16)[lane] = reinterpret_cast<const uint32_t*>(src + n16 * 16)[lane];
+    }
+  }
+}
+
+__device__ __forceinline__ float load_scale(const uint8_t* p) {
+  const uint32_t v = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
+                     (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
+  return __uint_as_float(v);
+}
+
+__device__ __forceinline__ void write_row_ids(const BatchArgs& a, int64_t s, uint32_t pos, uint32_t first) {
+  const int64_t c = s / a.chunk;
+  a.token_ids[pos] = static_cast<int32_t>(s);
+  a.offsets[pos] = static_cast<int32_t>(pos - first);
+  a.session_out[pos] = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
+  a.mb_out[pos] = a.micro_batch_ids ? a.micro_batch_ids[c] : 0;
+  if (a.dyn_scale != nullptr) a.dyn_scale[pos] = load_scale(a.scale_base + s * a.scale_stride);
+}
+
+// One wavefront per source slot (4 slots per workgroup).  The slot's output row is
+// scanned[key*nt + tile] + rank; its group's first row is scanned[key*nt].
+template <int VEC>
+__global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, const uint32_t* __restrict__ packed,
+                                                              const uint32_t* __restrict__ off, int nt,
+                                                              int tile_shift) {
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (s >= a.Y) return;
+  const uint32_t p = uniform(packed[s]);
+  if (p == kNoRank) return;
+  const uint32_t key = p >> 16;
+  const uint32_t pos = uniform(off[static_cast<int64_t>(key) * nt + (s >> tile_shift)]) + (p & 0xffffu);
+  const uint32_t lane = lane_id();
+  if (lane == 0) write_row_ids(a, s, pos, off[static_cast<int64_t>(key) * nt]);
+  copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+}
+
+// All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
+// LDS: u16 counters [4][nbp] | u32 key starts [nb + 1] | u32 output row of each slot [1024].
+template <int VEC>
+__global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nbits, int nb, int64_t* group_list,
+                                                             int64_t group_rows, int64_t* actual,
+                                                             int32_t* err_count) {
+  constexpr int R = 4;
+  extern __shared__ uint32_t lds_words[];
+  __shared__ uint32_t wsum[kRankThreads / kWave + 1];
+  __shared__ uint32_t err_w[kRankWaves];
+  const int nbp = rank_lds_stride(nb);
+  uint16_t* hist = reinterpret_cast<uint16_t*>(lds_words);
+  uint32_t* start = lds_words + kRankWaves * nbp / 2;
+  uint32_t* pos_of = start + nb + 1;
+  lds_zero_words(lds_words, kRankWaves * nbp / 2);
+  __syncthreads();
+
+  KeyBatching ks{a};
+  const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
+  const uint32_t lane = lane_id();
+  uint32_t dig[R], rank[R];
+  bool val[R];
+  uint32_t nerr = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
+    bool v = false, e = false;
+    uint32_t key = 0;
+    if (s < a.Y) key = ks.key(s, v, e);
+    dig[r] = key;
+    val[r] = v;
+    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e)));
+  }
+  rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
+  if (lane == 0) err_w[w] = nerr;
+  __syncthreads();
+  for (int k = threadIdx.x; k < nb; k += kRankThreads) {
+    uint32_t run = 0;
+#pragma unroll
+    for (int ww = 0; ww < kRankWaves; ++ww) {
+      const uint32_t c = hist[ww * nbp + k];
+      hist[ww * nbp + k] = static_cast<uint16_t>(run);
+      run += c;
+    }
+    start[k] = run;
+  }
+  __syncthreads();
+  // start[k] <- first output row of key k; group_list in the same sweep.
+  uint32_t carry = 0, gcarry = 0;
+  for (int k0 = 0; k0 < nb; k0 += kRankThreads) {
+    const int k = k0 + threadIdx.x;
+    const uint32_t cnt = (k < nb) ? start[k] : 0u;
+    uint32_t tot, present;
+    const uint32_t ex = block_exscan<kRankThreads>(cnt, wsum, tot);
+    const uint32_t slot = gcarry + block_exscan<kRankThreads>(cnt > 0 ? 1u : 0u, wsum, present);
+    if (k < nb) start[k] = carry + ex;
+    if (cnt > 0) {
+      group_list[2 * static_cast<int64_t>(slot)] = k;
+      group_list[2 * static_cast<int64_t>(slot) + 1] = cnt;
+    }
+    carry += tot;
+    gcarry += present;
+  }
+  for (int64_t g = gcarry + threadIdx.x; g < group_rows; g += kRankThreads) {
+    group_list[2 * g] = 0;
+    group_list[2 * g + 1] = 0;
+  }
+  if (threadIdx.x == 0) {
+    *actual = static_cast<int64_t>(carry);
+    if (err_count != nullptr) *err_count = static_cast<int32_t>(err_w[0] + err_w[1] + err_w[2] + err_w[3]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
+    if (s < a.Y) pos_of[s] = val[r] ? start[dig[r]] + hist[w * nbp + dig[r]] + rank[r] : kNoRank;
+  }
+  __syncthreads();
+  for (int64_t s = w; s < a.Y; s += kRankWaves) {
+    const uint32_t pos = pos_of[s];
+    if (pos == kNoRank) continue;
+    if (lane == 0) {
+      bool v, e;
+      const uint32_t key = ks.key(s, v, e);
+      write_row_ids(a, s, pos, start[key]);
+    }
+    copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+SortPass make_pass(int64_t n, int nb, int nbits, int shift) {
+  SortPass p;
+  p.n = n;
+  p.nb = nb;
+  p.nbits = nbits;
+  p.shift = shift;
+  const int64_t tiles4 = (n + 1023) / 1024;
+  p.R = (static_cast<int64_t>(nb) * tiles4 <= 65536) ? 4 : 16;
+  const int64_t tile = 256 * p.R;
+  p.nt = static_cast<int>((n + tile - 1) / tile);
+  p.tile_shift = (p.R == 4) ? 10 : 12;
+  return p;
+}
+
+SortPlan make_sort_plan(int64_t n, uint64_t nkeys) {
+  SortPlan sp;
+  if (nkeys <= 1) nkeys = 1;
+  const int B = bits_for(nkeys - 1);
+  if (nkeys <= static_cast<uint64_t>(kMaxSinglePassBuckets)) {
+    sp.npasses = 1;
+    sp.pass[0] = make_pass(n, static_cast<int>(nkeys), B, 0);
+  } else {
+    int P = (B + 12) / 13;
+    if (P < 2) P = 2;
+    const int D = (B + P - 1) / P;
+    sp.npasses = P;
+    for (int i = 0; i < P; ++i) {
+      const int shift = i * D;
+      const int bits = (shift + D <= B) ? D : (B - shift);
+      const uint64_t top = ((nkeys - 1) >> shift);
+      const int nb = (i == P - 1) ? static_cast<int>(top + 1) : (1 << bits);
+      sp.pass[i] = make_pass(n, nb, bits, shift);
+    }
+  }
+  for (int i = 0; i < sp.npasses; ++i) {
+    const int64_t w = static_cast<int64_t>(sp.pass[i].nb) * sp.pass[i].nt;
+    if (w > sp.hist_words) sp.hist_words = w;
+  }
+  return sp;
+}
+
+static int vec_class(uintptr_t a, uintptr_t b, int64_t s1, int64_t s2, int64_t bytes) {
+  const uint64_t m = static_cast<uint64_t>(a | b | static_cast<uint64_t>(s1) | static_cast<uint64_t>(s2) |
+                                           static_cast<uint64_t>(bytes));
+  if ((m & 15) == 0) return 16;
+  if ((m & 3) == 0) return 4;
+  return 1;
+}
+
+int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
+  if (d == nullptr || p == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  if (d->token_data == nullptr || d->expert_ids == nullptr || d->y == nullptr || d->session_ids_out == nullptr ||
+      d->micro_batch_ids_out == nullptr || d->token_ids == nullptr || d->expert_offsets == nullptr ||
+      d->group_list == nullptr || d->actual_token_num == nullptr)
+    return FFNWB_ERR_PARAM_NULLPTR;
+  if (d->token_dtype != FFNWB_DT_FP16 && d->token_dtype != FFNWB_DT_BF16 && d->token_dtype != FFNWB_DT_INT8)
+    return FFNWB_ERR_PARAM_INVALID;
+  const bool int8 = d->token_dtype == FFNWB_DT_INT8;
+  if (int8 && d->dynamic_scale == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  if (d->need_schedule != 0) return FFNWB_ERR_PARAM_INVALID;
+  if (d->expert_num <= 0 || d->expert_num > kMaxExperts) return FFNWB_ERR_PARAM_INVALID;
+  if (d->A <= 0 || d->A > 1024 || d->BS <= 0 || d->K1 <= 0 || d->K1 > 64 || d->H <= 0)
+    return FFNWB_ERR_PARAM_INVALID;
+  if (d->layer_num < 0 || d->layer_num > d->expert_num) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t L = d->layer_num > 1 ? d->layer_num : 1;
+  if (d->expert_num % L != 0) return FFNWB_ERR_PARAM_INVALID;
+  if (d->BS > (int64_t{1} << 31) / (d->A * d->K1)) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t Y = d->A * d->BS * d->K1;
+  if (Y >= (int64_t{1} << 31)) return FFNWB_ERR_PARAM_INVALID;
+  if (d->H > (int64_t{1} << 40)) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t row = d->H * (int8 ? 1 : 2);
+  const bool packed_scale = int8 && d->token_scale == nullptr;
+  const int64_t min_stride = row + (packed_scale ? 4 : 0);
+  const int64_t stride = d->token_row_stride ? d->token_row_stride : min_stride;
+  if (stride < min_stride) return FFNWB_ERR_PARAM_INVALID;
+  if (int8 && !packed_scale && d->scale_stride < 0) return FFNWB_ERR_PARAM_INVALID;
+  // output rows are addressed with 32-bit row numbers times the row size
+  if (static_cast<double>(Y) * static_cast<double>(stride) > 9.0e18) return FFNWB_ERR_PARAM_INVALID;
+
+  p->Y = Y;
+  p->row_bytes = row;
+  p->stride = stride;
+  if (int8) {
+    if (packed_scale) {
+      p->scale_base = static_cast<const uint8_t*>(d->token_data) + row;
+      p->scale_stride = stride;
+    } else {
+      p->scale_base = reinterpret_cast<const uint8_t*>(d->token_scale);
+      p->scale_stride = d->scale_stride ? d->scale_stride : 4;
+    }
+  }
+  const int nb = static_cast<int>(d->expert_num);
+  p->pass = make_pass(Y, nb, bits_for(static_cast<uint64_t>(nb - 1)), 0);
+  p->vec = vec_class(reinterpret_cast<uintptr_t>(d->token_data), reinterpret_cast<uintptr_t>(d->y), stride, row, row);
+  p->small = (p->pass.nt == 1) && p->pass.R == 4 && nb <= 4096 && Y * row <= (int64_t{1} << 22);
+  if (p->small) {
+    p->ws_bytes = 0;
+  } else {
+    Carve c;
+    c.take<uint32_t>(Y);                                              // packed digit / rank
+    c.take<uint32_t>(static_cast<size_t>(nb) * p->pass.nt);           // histogram -> offsets
+    c.take<uint32_t>(p->pass.nt);                                     // per-tile bad-id counts
+    p->ws_bytes = c.off;
+  }
+  return FFNWB_OK;
+}
+
+template <class F>
+static hipError_t launch_vec(int vec, F&& f) {
+  if (vec == 16) f(std::integral_constant<int, 16>());
+  else if (vec == 4) f(std::integral_constant<int, 4>());
+  else f(std::integral_constant<int, 1>());
+  return hipGetLastError();
+}
+
+int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s) {
+  BatchArgs a{};
+  a.Y = p.Y;
+  a.chunk = d->BS * d->K1;
+  a.L = static_cast<int32_t>(d->layer_num > 1 ? d->layer_num : 1);
+  a.per_layer = static_cast<int32_t>(d->expert_num / a.L);
+  a.layer_num = static_cast<int32_t>(d->layer_num);
+  a.expert_ids = d->expert_ids;
+  a.mask = d->mask;
+  a.layer_ids = d->layer_ids;
+  a.session_ids = d->session_ids;
+  a.micro_batch_ids = d->micro_batch_ids;
+  a.token_data = static_cast<const uint8_t*>(d->token_data);
+  a.stride = p.stride;
+  a.scale_base = p.scale_base;
+  a.scale_stride = p.scale_stride;
+  a.y = static_cast<uint8_t*>(d->y);
+  a.row_bytes = p.row_bytes;
+  a.session_out = d->session_ids_out;
+  a.mb_out = d->micro_batch_ids_out;
+  a.token_ids = d->token_ids;
+  a.offsets = d->expert_offsets;
+  a.dyn_scale = (d->token_dtype == FFNWB_DT_INT8) ? d->dynamic_scale : nullptr;
+  const int nb = p.pass.nb;
+  hipError_t err = hipSuccess;
+
+  if (p.small) {
+    const size_t lds = rank_lds_bytes(nb) + (static_cast<size_t>(nb) + 1 + 1024) * sizeof(uint32_t);
+    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
+    err = launch_vec(p.vec, [&](auto v) {
+      hipLaunchKernelGGL(batching_small_kernel<decltype(v)::value>, dim3(1), dim3(kRankThreads), lds, s, a,
+                         p.pass.nbits, nb, d->group_list, d->expert_num, d->actual_token_num, d->err_count);
+    });
+    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+  }
+
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  uint32_t* packed = c.take<uint32_t>(p.Y);
+  uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(nb) * p.pass.nt);
+  uint32_t* tile_err = c.take<uint32_t>(p.pass.nt);
+
+  KeyBatching ks{a};
+  const size_t lds = rank_lds_bytes(nb);
+  allow_large_lds(reinterpret_cast<const void*>(p.pass.R == 4 ? &sort_rank_kernel<4, KeyBatching>
+                                                               : &sort_rank_kernel<16, KeyBatching>), lds);
+  if (p.pass.R == 4)
+    hipLaunchKernelGGL((sort_rank_kernel<4, KeyBatching>), dim3(p.pass.nt), dim3(kRankThreads), lds, s, ks, p.Y, 0,
+                       p.pass.nbits, nb, packed, hist, p.pass.nt, tile_err);
+  else
+    hipLaunchKernelGGL((sort_rank_kernel<16, KeyBatching>), dim3(p.pass.nt), dim3(kRankThreads), lds, s, ks, p.Y, 0,
+                       p.pass.nbits, nb, packed, hist, p.pass.nt, tile_err);
+  if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+
+  ScanTail tail{d->group_list, d->expert_num, d->actual_token_num, d->err_count, tile_err};
+  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), 0, s, hist,
+                     static_cast<int64_t>(nb) * p.pass.nt, static_cast<uint32_t*>(nullptr),
+                     static_cast<uint32_t*>(nullptr), nb, p.pass.nt, tail);
+  if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+
+  if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
+  const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+  err = launch_vec(p.vec, [&](auto v) {
+    hipLaunchKernelGGL(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, packed, hist,
+                       p.pass.nt, p.pass.tile_shift);
+  });
+  if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+  return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+}
+
+}  // namespace ffnwb

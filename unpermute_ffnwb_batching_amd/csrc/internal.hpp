@@ -1,0 +1,102 @@
+// Host-side plans and launchers shared by the API layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ffnwb.h"
+
+namespace ffnwb {
+
+// gfx950 lets one workgroup address all 160 KiB of a CU's LDS.
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+// A single counting-sort pass holds 4 waves x nb u16 counters in LDS.
+constexpr int kMaxSinglePassBuckets = 20480;
+constexpr int kMaxExperts = 8192;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int bits_for(uint64_t max_value) {  // bits needed to represent values <= max_value
+  int b = 0;
+  while (b < 64 && (max_value >> b) != 0) ++b;
+  return b;
+}
+
+// Workspace carve-out helper: records offsets while sizing, hands out pointers while launching.
+struct Carve {
+  size_t off = 0;
+  char* base = nullptr;
+  template <class T>
+  T* take(size_t count) {
+    const size_t o = off;
+    off = align_up(off + count * sizeof(T), 256);
+    return base ? reinterpret_cast<T*>(base + o) : nullptr;
+  }
+};
+
+// One stable counting-sort pass over n elements with nb buckets.
+struct SortPass {
+  int64_t n = 0;
+  int nb = 0;        // buckets of this pass
+  int nbits = 0;     // digit width (ballot rounds)
+  int shift = 0;     // digit = (key >> shift) & ((1 << nbits) - 1)
+  int R = 4;         // rounds per wave: tile = 256 * R elements
+  int nt = 0;        // tiles
+  int tile_shift = 0;
+};
+
+SortPass make_pass(int64_t n, int nb, int nbits, int shift);
+
+// A full stable sort of n keys in [0, nkeys): one pass when nkeys fits in LDS, else LSD passes.
+struct SortPlan {
+  int npasses = 0;
+  SortPass pass[4];
+  int64_t hist_words = 0;  // largest nb * nt over the passes
+};
+
+SortPlan make_sort_plan(int64_t n, uint64_t nkeys);
+
+struct BatchingPlan {
+  int64_t Y = 0;
+  int64_t row_bytes = 0;
+  int64_t stride = 0;
+  const uint8_t* scale_base = nullptr;
+  int64_t scale_stride = 0;
+  bool small = false;  // single fused workgroup
+  SortPass pass;
+  int vec = 16;        // row copy width class: 16, 4 or 1
+  size_t ws_bytes = 0;
+};
+
+int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p);
+int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s);
+
+struct UnpermutePlan {
+  int64_t T = 0, H = 0, N = 0, E = 0, rows = 0, K = 0, C = 0;
+  bool has_probs = false;
+  bool padded = false;
+  int elt = 0, pelt = 0;
+  bool need_aux = false;     // out_index / permute_token_id requested (non-padded)
+  SortPass mask_pass;        // non-padded probs compaction
+  SortPlan sort;             // padded inversion, or non-padded auxiliary order
+  size_t ws_bytes = 0;
+};
+
+int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p);
+int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* ws, hipStream_t s);
+
+bool log_enabled();
+
+// Records an optional timing event (a hipEvent_t passed as void*) on stream s.
+inline bool record_event(void* ev, hipStream_t s) {
+  return ev == nullptr || hipEventRecord(static_cast<hipEvent_t>(ev), s) == hipSuccess;
+}
+void log_warn(const char* fmt, ...);
+
+// Allows a kernel to be launched with more than 64 KiB of dynamic LDS (gfx950: up to 160 KiB).
+inline void allow_large_lds(const void* kernel, size_t bytes) {
+  if (bytes > 32768) (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+}  // namespace ffnwb
