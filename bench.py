@@ -174,6 +174,10 @@ def main():
     K, W = args.steps, args.warmup
     have_np = "unpermute_nonpadded" in calls
     hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for b, e in hot:  # torch creates the HIP event on its first record; the library records it again
+        b.record(stream)
+        e.record(stream)
+    torch.cuda.synchronize()
 
     def step(i=None):
         for n, call in calls.items():

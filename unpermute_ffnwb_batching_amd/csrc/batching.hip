@@ -44,7 +44,7 @@ struct KeyBatching {
   __device__ uint32_t key(int64_t s, bool& valid, bool& err) const {
     valid = false; err = false;
     if (a.mask != nullptr && a.mask[s] != 0) return 0;
-    const int64_t c = s / a.chunk;
+    const uint32_t c = static_cast<uint32_t>(s) / static_cast<uint32_t>(a.chunk);
     const int32_t layer = (a.layer_ids != nullptr && a.layer_num >= 1) ? a.layer_ids[c] : 0;
     const int32_t e = a.expert_ids[s];
     if (e < 0 || e >= a.per_layer || layer < 0 || layer >= a.L) { err = true; return 0; }
@@ -53,32 +53,50 @@ struct KeyBatching {
   }
 };
 
-// Copies one row with the calling wavefront.  VEC = 16: every address 16-byte aligned;
-// VEC = 4: 4-byte aligned (16-byte accesses at dword alignment, dword tail); VEC = 1: bytes.
+// Row copies by one wavefront.  VEC = 16: every address 16-byte aligned; VEC = 4: 4-byte
+// aligned (16-byte accesses at dword alignment plus a dword tail); VEC = 1: bytes.  A row
+// moves in pieces of kPiece 16-byte accesses per lane (16 KiB per wave); the loads of a
+// piece are all issued before its first store.
+constexpr int kPiece = 16;
+
+template <int VEC> struct RowVec { typedef u32x4 type; };
+template <> struct RowVec<4> { typedef u32x4_a4 type; };
+
 template <int VEC>
-__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t bytes,
-                                         uint32_t lane) {
-  constexpr int U = 8;
+struct RowPiece {
+  typedef typename RowVec<VEC>::type V;
+  V v[kPiece];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ src, int64_t n16, int64_t b, uint32_t lane) {
+    const V* s4 = reinterpret_cast<const V*>(src);
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) v[u] = __builtin_nontemporal_load(s4 + i);  // streamed once: do not keep in cache
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* __restrict__ dst, int64_t n16, int64_t b, uint32_t lane) const {
+    V* d4 = reinterpret_cast<V*>(dst);
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) __builtin_nontemporal_store(v[u], d4 + i);
+    }
+  }
+};
+
+// Copies bytes [from, bytes) of a row (the part not moved by an earlier piece).
+template <int VEC>
+__device__ __forceinline__ void copy_row_rest(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                              int64_t bytes, int64_t from16, uint32_t lane) {
   if (VEC == 1) {
     for (int64_t i = lane; i < bytes; i += kWave) dst[i] = src[i];
     return;
   }
-  typedef typename std::conditional<VEC == 16, u32x4, u32x4_a4>::type V;
-  const V* s4 = reinterpret_cast<const V*>(src);
-  V* d4 = reinterpret_cast<V*>(dst);
   const int64_t n16 = bytes >> 4;
-  for (int64_t b = 0; b < n16; b += kWave * U) {
-    V v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = b + u * kWave + lane;
-      if (i < n16) v[u] = s4[i];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = b + u * kWave + lane;
-      if (i < n16) d4[i] = v[u];
-    }
+  for (int64_t b = from16; b < n16; b += kWave * kPiece) {
+    RowPiece<VEC> piece;
+    piece.load(src, n16, b, lane);
+    piece.store(dst, n16, b, lane);
   }
   if (VEC == 4) {
     const int64_t tail = (bytes & 15) >> 2;
@@ -88,6 +106,12 @@ __device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_
   }
 }
 
+template <int VEC>
+__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t bytes,
+                                         uint32_t lane) {
+  copy_row_rest<VEC>(src, dst, bytes, 0, lane);
+}
+
 __device__ __forceinline__ float load_scale(const uint8_t* p) {
   const uint32_t v = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
                      (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
@@ -95,7 +119,7 @@ __device__ __forceinline__ float load_scale(const uint8_t* p) {
 }
 
 __device__ __forceinline__ void write_row_ids(const BatchArgs& a, int64_t s, uint32_t pos, uint32_t first) {
-  const int64_t c = s / a.chunk;
+  const uint32_t c = static_cast<uint32_t>(s) / static_cast<uint32_t>(a.chunk);
   a.token_ids[pos] = static_cast<int32_t>(s);
   a.offsets[pos] = static_cast<int32_t>(pos - first);
   a.session_out[pos] = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
@@ -104,20 +128,34 @@ __device__ __forceinline__ void write_row_ids(const BatchArgs& a, int64_t s, uin
 }
 
 // One wavefront per source slot (4 slots per workgroup).  The slot's output row is
-// scanned[key*nt + tile] + rank; its group's first row is scanned[key*nt].
+// start[key] + off[tile*nb + key] + rank; its group's first row is start[key].  The first
+// piece of the source row is loaded before that lookup, so the lookup's latency hides
+// under the row loads.
 template <int VEC>
 __global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, const uint32_t* __restrict__ packed,
-                                                              const uint32_t* __restrict__ off, int nt,
+                                                              const uint32_t* __restrict__ off,
+                                                              const uint32_t* __restrict__ start, int nb,
                                                               int tile_shift) {
   const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
   if (s >= a.Y) return;
   const uint32_t p = uniform(packed[s]);
   if (p == kNoRank) return;
-  const uint32_t key = p >> 16;
-  const uint32_t pos = uniform(off[static_cast<int64_t>(key) * nt + (s >> tile_shift)]) + (p & 0xffffu);
   const uint32_t lane = lane_id();
-  if (lane == 0) write_row_ids(a, s, pos, off[static_cast<int64_t>(key) * nt]);
-  copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+  const uint8_t* src = a.token_data + s * a.stride;
+  const int64_t n16 = a.row_bytes >> 4;
+  RowPiece<VEC> first;
+  if (VEC != 1) first.load(src, n16, 0, lane);
+  const uint32_t key = p >> 16;
+  const uint32_t gstart = uniform(start[key]);
+  const uint32_t pos = gstart + uniform(off[(s >> tile_shift) * nb + key]) + (p & 0xffffu);
+  uint8_t* dst = a.y + static_cast<int64_t>(pos) * a.row_bytes;
+  if (VEC != 1) {
+    first.store(dst, n16, 0, lane);
+    copy_row_rest<VEC>(src, dst, a.row_bytes, kWave * kPiece, lane);
+  } else {
+    copy_row_rest<VEC>(src, dst, a.row_bytes, 0, lane);
+  }
+  if (lane == 0) write_row_ids(a, s, pos, gstart);
 }
 
 // All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
@@ -249,6 +287,7 @@ SortPlan make_sort_plan(int64_t n, uint64_t nkeys) {
   for (int i = 0; i < sp.npasses; ++i) {
     const int64_t w = static_cast<int64_t>(sp.pass[i].nb) * sp.pass[i].nt;
     if (w > sp.hist_words) sp.hist_words = w;
+    if (sp.pass[i].nb > sp.max_nb) sp.max_nb = sp.pass[i].nb;
   }
   return sp;
 }
@@ -313,6 +352,7 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
     Carve c;
     c.take<uint32_t>(Y);                                              // packed digit / rank
     c.take<uint32_t>(static_cast<size_t>(nb) * p->pass.nt);           // histogram -> offsets
+    c.take<uint32_t>(static_cast<size_t>(nb) + 1);                    // key starts
     c.take<uint32_t>(p->pass.nt);                                     // per-tile bad-id counts
     p->ws_bytes = c.off;
   }
@@ -368,6 +408,7 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   c.base = static_cast<char*>(ws);
   uint32_t* packed = c.take<uint32_t>(p.Y);
   uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(nb) * p.pass.nt);
+  uint32_t* kstart = c.take<uint32_t>(static_cast<size_t>(nb) + 1);
   uint32_t* tile_err = c.take<uint32_t>(p.pass.nt);
 
   KeyBatching ks{a};
@@ -383,16 +424,17 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   ScanTail tail{d->group_list, d->expert_num, d->actual_token_num, d->err_count, tile_err};
-  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), 0, s, hist,
-                     static_cast<int64_t>(nb) * p.pass.nt, static_cast<uint32_t*>(nullptr),
-                     static_cast<uint32_t*>(nullptr), nb, p.pass.nt, tail);
+  const size_t scan_lds = static_cast<size_t>(nb) * sizeof(uint32_t);
+  allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), scan_lds);
+  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), scan_lds, s, hist, nb, p.pass.nt, kstart,
+                     static_cast<uint32_t*>(nullptr), tail);
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
   const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
   err = launch_vec(p.vec, [&](auto v) {
     hipLaunchKernelGGL(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, packed, hist,
-                       p.pass.nt, p.pass.tile_shift);
+                       kstart, nb, p.pass.tile_shift);
   });
   if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
   return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;

@@ -53,6 +53,7 @@ struct SortPlan {
   int npasses = 0;
   SortPass pass[4];
   int64_t hist_words = 0;  // largest nb * nt over the passes
+  int max_nb = 0;          // largest nb over the passes
 };
 
 SortPlan make_sort_plan(int64_t n, uint64_t nkeys);
@@ -78,7 +79,7 @@ struct UnpermutePlan {
   bool padded = false;
   int elt = 0, pelt = 0;
   bool need_aux = false;     // out_index / permute_token_id requested (non-padded)
-  SortPass mask_pass;        // non-padded probs compaction
+  int64_t mask_tiles = 0;    // non-padded probs compaction: token tiles
   SortPlan sort;             // padded inversion, or non-padded auxiliary order
   size_t ws_bytes = 0;
 };

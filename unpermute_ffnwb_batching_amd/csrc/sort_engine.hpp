@@ -1,8 +1,8 @@
 // Stable counting sort on CDNA4, used by every ordering step of the library:
 //   - batching: slots keyed by (layer, expert)              (one pass, <= 8192 buckets)
 //   - unpermute, padded: capacity entries keyed by token     (one pass while T+1 <= 20480)
-//   - unpermute, non-padded: probs compaction keyed by expert, and the auxiliary
-//     out_index ordering keyed by sortedIndices (LSD passes when the key range is large)
+//   - unpermute, non-padded: the auxiliary out_index ordering keyed by sortedIndices
+//     (LSD passes when the key range is large)
 //
 // A pass over n elements splits them into tiles of 256*R consecutive elements, one
 // 256-thread workgroup (4 waves) per tile.  Wave w owns the contiguous sub-range
@@ -12,10 +12,10 @@
 // wave's private LDS counter of that digit, and every lane's rank is the counter's old
 // value plus the number of equal-digit lanes below it.  After a barrier, a per-digit
 // prefix over the 4 waves turns the per-wave counters into per-wave bases and gives the
-// tile's digit histogram, written bucket-major to global memory (hist[digit*nt + tile]).
-// One workgroup then exclusive-scans that bucket-major matrix in place, which yields,
-// for every (digit, tile), the first output position of that tile's run of the digit.
-// Element j's output position is scanned[digit*nt + tile] + rank: ties keep input order.
+// tile's digit histogram, written tile-major (hist[tile*nb + digit], coalesced).
+// One workgroup then turns every digit's column of that matrix into an exclusive prefix
+// over tiles (in place) and scans the digit totals into start[digit].  Element j's output
+// position is start[digit] + hist[tile*nb + digit] + rank: ties keep input order.
 #pragma once
 
 #include "device_common.hpp"
@@ -111,15 +111,6 @@ struct KeyNonPadded {
   }
 };
 
-// Probs compaction: element j = t*E + e takes part iff routing_map[j] != 0; key = e.
-struct KeyRoutingMap {
-  const uint8_t* map; int32_t E;
-  __device__ uint32_t key(int64_t j, bool& valid, bool& err) const {
-    valid = map[j] != 0; err = false;
-    return static_cast<uint32_t>(static_cast<uint32_t>(j) % static_cast<uint32_t>(E));
-  }
-};
-
 // Later LSD passes: keys already materialised.
 struct KeyArray {
   const uint32_t* keys;
@@ -127,7 +118,7 @@ struct KeyArray {
 };
 
 // ------------------------------------------------------------------ ranking pass
-// packed[j] = pack_rank(digit, rank within tile) or kNoRank; hist_g[d*nt + tile] = count.
+// packed[j] = pack_rank(digit, rank within tile) or kNoRank; hist_g[tile*nb + d] = count.
 // tile_err[tile] = number of elements with err set (if tile_err != nullptr).
 template <int R, class KS>
 __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t n, int shift, int nbits, int nb,
@@ -169,7 +160,7 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
       hist[ww * nbp + k] = static_cast<uint16_t>(run);
       run += c;
     }
-    hist_g[static_cast<int64_t>(k) * nt + blockIdx.x] = run;
+    hist_g[static_cast<int64_t>(blockIdx.x) * nb + k] = run;
   }
   if (tile_err != nullptr && threadIdx.x == 0)
     tile_err[blockIdx.x] = err_w[0] + err_w[1] + err_w[2] + err_w[3];
@@ -182,12 +173,12 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
 }
 
 // ------------------------------------------------------------------ scan of the histogram
-// In-place exclusive scan of a[0..n) by one 1024-thread workgroup; each thread scans one
-// contiguous chunk.  Optional outputs:
-//   total_out[0]      = sum of all entries
-//   bucket_start[k]   = a[k*nt] after the scan, for k < nb; bucket_start[nb] = total
-//   batching tail     = compact group_list rows {k, count_k} for count_k > 0, {0,0} after,
-//                       actual_token_num, and err_count = sum of tile_err[0..nt).
+// One 1024-thread workgroup.  Phase 1: thread k walks digit k's column of the tile-major
+// histogram (coalesced across threads), replacing each count by the number of elements
+// with that digit in earlier tiles, and keeps the digit's total in LDS.  Phase 2: an
+// exclusive scan of the totals gives start[k] (start[nb] = n placed).  Optional tail for
+// batching: compact group_list rows {k, count_k} for count_k > 0 then {0,0},
+// actual_token_num and err_count = sum of tile_err[0..nt).
 struct ScanTail {
   int64_t* group_list;    // nullptr = no batching tail
   int64_t group_rows;
@@ -196,40 +187,57 @@ struct ScanTail {
   const uint32_t* tile_err;
 };
 
-static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t* __restrict__ a, int64_t n,
-                                                                 uint32_t* __restrict__ total_out,
-                                                                 uint32_t* __restrict__ bucket_start, int nb, int nt,
-                                                                 ScanTail tail) {
+constexpr int kScanMaxBuckets = 20480;  // LDS holds every digit total (80 KiB)
+
+static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t* __restrict__ h, int nb, int nt,
+                                                                        uint32_t* __restrict__ start,
+                                                                        uint32_t* __restrict__ total_out,
+                                                                        ScanTail tail) {
+  extern __shared__ uint32_t tot[];  // [nb]
   __shared__ uint32_t wsum[kScanThreads / kWave + 1];
-  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = min(n, static_cast<int64_t>(threadIdx.x) * per);
-  const int64_t hi = min(n, lo + per);
-  uint32_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += a[i];
-  uint32_t total;
-  uint32_t pre = block_exscan<kScanThreads>(s, wsum, total);
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint32_t v = a[i];
-    a[i] = pre;
-    pre += v;
+  for (int k = threadIdx.x; k < nb; k += kScanThreads) {
+    uint32_t run = 0;
+    int t = 0;
+    for (; t + 8 <= nt; t += 8) {
+      uint32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = h[static_cast<int64_t>(t + u) * nb + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        h[static_cast<int64_t>(t + u) * nb + k] = run;
+        run += c[u];
+      }
+    }
+    for (; t < nt; ++t) {
+      const uint32_t c = h[static_cast<int64_t>(t) * nb + k];
+      h[static_cast<int64_t>(t) * nb + k] = run;
+      run += c;
+    }
+    tot[k] = run;
   }
-  if (threadIdx.x == 0 && total_out != nullptr) *total_out = total;
-  if (bucket_start == nullptr && tail.group_list == nullptr) return;
   __syncthreads();
-  if (bucket_start != nullptr) {
-    for (int k = threadIdx.x; k < nb; k += kScanThreads) bucket_start[k] = a[static_cast<int64_t>(k) * nt];
-    if (threadIdx.x == 0) bucket_start[nb] = total;
+  // exclusive scan of tot[0..nb): thread i owns the contiguous run [i*per, (i+1)*per)
+  const int per = (nb + kScanThreads - 1) / kScanThreads;
+  const int lo = min(nb, static_cast<int>(threadIdx.x) * per);
+  const int hi = min(nb, lo + per);
+  uint32_t sum = 0;
+  for (int k = lo; k < hi; ++k) sum += tot[k];
+  uint32_t total;
+  uint32_t pre = block_exscan<kScanThreads>(sum, wsum, total);
+  for (int k = lo; k < hi; ++k) {
+    start[k] = pre;
+    pre += tot[k];
+  }
+  if (threadIdx.x == 0) {
+    start[nb] = total;
+    if (total_out != nullptr) *total_out = total;
   }
   if (tail.group_list == nullptr) return;
+  __syncthreads();
   uint32_t carry = 0;
   for (int k0 = 0; k0 < nb; k0 += kScanThreads) {
     const int k = k0 + threadIdx.x;
-    uint32_t cnt = 0;
-    if (k < nb) {
-      const uint32_t s0 = a[static_cast<int64_t>(k) * nt];
-      const uint32_t s1 = (k + 1 < nb) ? a[static_cast<int64_t>(k + 1) * nt] : total;
-      cnt = s1 - s0;
-    }
+    const uint32_t cnt = (k < nb) ? tot[k] : 0u;
     uint32_t present;
     const uint32_t slot = carry + block_exscan<kScanThreads>(cnt > 0 ? 1u : 0u, wsum, present);
     if (cnt > 0) {
@@ -254,11 +262,12 @@ static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t
 
 // Output position of element j after a ranking pass and the scan (false if not placed).
 __device__ __forceinline__ bool placed_position(const uint32_t* __restrict__ packed, const uint32_t* __restrict__ off,
-                                                int nt, int tile_shift, int64_t j, uint32_t& pos, uint32_t& digit) {
+                                                const uint32_t* __restrict__ start, int nb, int tile_shift,
+                                                int64_t j, uint32_t& pos, uint32_t& digit) {
   const uint32_t p = packed[j];
   if (p == kNoRank) return false;
   digit = p >> 16;
-  pos = off[static_cast<int64_t>(digit) * nt + (j >> tile_shift)] + (p & 0xffffu);
+  pos = start[digit] + off[(j >> tile_shift) * nb + digit] + (p & 0xffffu);
   return true;
 }
 
@@ -269,7 +278,8 @@ __device__ __forceinline__ bool placed_position(const uint32_t* __restrict__ pac
 template <class KS, bool FIRST, int FINAL>
 __global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t* __restrict__ vals_in,
                                                           const uint32_t* __restrict__ packed,
-                                                          const uint32_t* __restrict__ off, int nt, int tile_shift,
+                                                          const uint32_t* __restrict__ off,
+                                                          const uint32_t* __restrict__ start, int nb, int tile_shift,
                                                           int64_t n, uint32_t* __restrict__ keys_out,
                                                           uint32_t* __restrict__ vals_out,
                                                           int32_t* __restrict__ out_index,
@@ -278,7 +288,7 @@ __global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t*
   const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j >= n) return;
   uint32_t pos, digit;
-  if (!placed_position(packed, off, nt, tile_shift, j, pos, digit)) return;
+  if (!placed_position(packed, off, start, nb, tile_shift, j, pos, digit)) return;
   bool v, e;
   const uint32_t key = ks.key(j, v, e);
   const uint32_t val = FIRST ? static_cast<uint32_t>(j) : vals_in[j];

@@ -36,11 +36,105 @@ struct ReduceArgs {
   uint8_t* out;
 };
 
-// One workgroup per token.  Each thread owns 16-byte chunks of the hidden dimension
-// (VEC) or single elements; the token's (row, weight) entries are uniform across the
-// workgroup and are fetched 8 at a time so that 8 row loads are in flight per thread.
-template <class TT, class TW, int MODE, bool VEC>
+// One workgroup per token; each thread owns CPT 16-byte chunks of the hidden dimension
+// (or single elements when rows are not 16-byte multiples).  Every wave fetches the
+// token's entry list itself, one entry per lane with a single coalesced load, and marks
+// the valid ones with a ballot; it then walks the valid entries in ascending order, 8 at
+// a time, broadcasting each row index with readlane so that the 8 x CPT row loads of a
+// batch are all in flight before the first one is used.  The weight of each entry is
+// gathered per lane before the row loads and read back with readlane after them.
+template <class TT, class TW, int MODE, int CPT>
 __global__ __launch_bounds__(1024) void unpermute_reduce_kernel(ReduceArgs a) {
+  constexpr bool kPadded = MODE >= kPad;
+  constexpr bool kHasW = (MODE == kNonPadW2) || (MODE == kNonPadW1) || (MODE == kPadW);
+  constexpr int VE = Chunk<TT>::kElems;
+  constexpr int B = 8;
+  const int64_t t = blockIdx.x;
+  const uint32_t lane = lane_id();
+  int64_t ebase, nent;
+  if (kPadded) {
+    ebase = uniform64(static_cast<int64_t>(a.seg[t]));
+    nent = uniform64(static_cast<int64_t>(a.seg[t + 1])) - ebase;
+  } else {
+    ebase = t * a.K;
+    nent = a.K;
+  }
+  const int64_t chunks = a.H * TT::kBytes / 16;
+  const u32x4* __restrict__ x4 = reinterpret_cast<const u32x4*>(a.x);
+  u32x4* __restrict__ o4 = reinterpret_cast<u32x4*>(a.out);
+  for (int64_t c0 = 0; c0 < chunks; c0 += static_cast<int64_t>(CPT) * blockDim.x) {
+    int64_t cidx[CPT];
+    bool cok[CPT];
+    float acc[CPT][VE];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      cidx[i] = c0 + threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+      cok[i] = cidx[i] < chunks;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[i][e] = 0.0f;
+    }
+    for (int64_t g = 0; g < nent; g += kWave) {
+      const int64_t k = g + lane;
+      int32_t r = 0;
+      bool ok = false;
+      if (k < nent) {
+        const int32_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
+        ok = kPadded || (idx >= 0 && idx < a.rows);
+        r = idx;
+      }
+      float wl = 1.0f;
+      if (kHasW && ok) wl = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : static_cast<int64_t>(r));
+      uint64_t vm = wave_ballot(ok);
+      while (vm != 0) {
+        int32_t rr[B];
+        int lsel[B];
+        int nb = 0;
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          rr[u] = 0;
+          lsel[u] = 0;
+          if (vm != 0) {
+            const int l = static_cast<int>(__builtin_ctzll(vm));
+            vm &= vm - 1;
+            lsel[u] = l;
+            rr[u] = __builtin_amdgcn_readlane(r, l);
+            nb = u + 1;
+          }
+        }
+        u32x4 xv[B][CPT];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          if (u < nb) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i)
+              if (cok[i]) xv[u][i] = __builtin_nontemporal_load(x4 + static_cast<int64_t>(rr[u]) * chunks + cidx[i]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          if (u < nb) {
+            const float w = kHasW ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), lsel[u])) : 1.0f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+              if (!cok[i]) continue;
+              float f[VE];
+              Chunk<TT>::widen(xv[u][i], f);
+#pragma unroll
+              for (int e = 0; e < VE; ++e) acc[i][e] = kHasW ? acc[i][e] + f[e] * w : acc[i][e] + f[e];
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (cok[i]) o4[t * chunks + cidx[i]] = Chunk<TT>::narrow(acc[i]);
+  }
+}
+
+// Element-wise variant for rows that are not a multiple of 16 bytes (or misaligned).
+template <class TT, class TW, int MODE>
+__global__ __launch_bounds__(1024) void unpermute_reduce_elem_kernel(ReduceArgs a) {
   constexpr bool kPadded = MODE >= kPad;
   constexpr bool kHasW = (MODE == kNonPadW2) || (MODE == kNonPadW1) || (MODE == kPadW);
   const int64_t t = blockIdx.x;
@@ -52,81 +146,72 @@ __global__ __launch_bounds__(1024) void unpermute_reduce_kernel(ReduceArgs a) {
     ebase = t * a.K;
     nent = a.K;
   }
-  constexpr int B = 8;
-  if (VEC) {
-    constexpr int VE = Chunk<TT>::kElems;
-    const int64_t chunks = a.H * TT::kBytes / 16;
-    const u32x4* __restrict__ x4 = reinterpret_cast<const u32x4*>(a.x);
-    u32x4* __restrict__ o4 = reinterpret_cast<u32x4*>(a.out);
-    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-      float acc[VE];
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
-      for (int64_t k0 = 0; k0 < nent; k0 += B) {
-        int64_t r[B];
-        float w[B];
-        bool ok[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int64_t k = k0 + u;
-          ok[u] = k < nent;
-          r[u] = 0;
-          w[u] = 1.0f;
-          if (ok[u]) {
-            const int64_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
-            if (!kPadded) ok[u] = idx >= 0 && idx < a.rows;
-            r[u] = idx;
-            if (ok[u] && kHasW) w[u] = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : idx);
-          }
-        }
-        u32x4 xv[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u)
-          if (ok[u]) xv[u] = x4[r[u] * chunks + c];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          if (!ok[u]) continue;
-          float f[VE];
-          Chunk<TT>::widen(xv[u], f);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[e] = kHasW ? acc[e] + f[e] * w[u] : acc[e] + f[e];
-        }
+  for (int64_t h = threadIdx.x; h < a.H; h += blockDim.x) {
+    float acc = 0.0f;
+    for (int64_t k = 0; k < nent; ++k) {
+      const int64_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
+      if (!kPadded && !(idx >= 0 && idx < a.rows)) continue;
+      const float f = load_elem<TT>(a.x, idx * a.H + h);
+      if (kHasW) {
+        const float w = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : idx);
+        acc = acc + f * w;
+      } else {
+        acc = acc + f;
       }
-      o4[t * chunks + c] = Chunk<TT>::narrow(acc);
     }
-  } else {
-    for (int64_t h = threadIdx.x; h < a.H; h += blockDim.x) {
-      float acc = 0.0f;
-      for (int64_t k = 0; k < nent; ++k) {
-        const int64_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
-        if (!kPadded && !(idx >= 0 && idx < a.rows)) continue;
-        const float f = load_elem<TT>(a.x, idx * a.H + h);
-        if (kHasW) {
-          const float w = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : idx);
-          acc = acc + f * w;
-        } else {
-          acc = acc + f;
-        }
-      }
-      store_elem<TT>(a.out, t * a.H + h, acc);
-    }
+    store_elem<TT>(a.out, t * a.H + h, acc);
   }
 }
 
-// Probs compaction scatter: permute_probs[pos(j)] = probs[j] for placed entries, then
-// zero from the number of placed entries up to N (entries beyond N are dropped).
-template <typename P>
-__global__ __launch_bounds__(256) void mask_scatter_kernel(const uint32_t* __restrict__ packed,
-                                                           const uint32_t* __restrict__ off, int nt, int tile_shift,
-                                                           int64_t n, const P* __restrict__ probs,
-                                                           P* __restrict__ pp, int64_t N,
-                                                           const uint32_t* __restrict__ total) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j < n) {
-    uint32_t pos, dig;
-    if (placed_position(packed, off, nt, tile_shift, j, pos, dig) && pos < N) pp[pos] = probs[j];
+// Probs compaction (non-padded with probs): permute_probs lists probs[t, e] for the
+// non-zero routing-map entries in expert-major order, i.e. a stable counting sort of
+// the entries t*E + e by e.  The map is cut into tiles of kMaskTile tokens; thread e of
+// a tile's workgroup walks column e of the tile, so within a column the tile's entries
+// are already in token order and their rank is a running count.
+constexpr int kMaskTile = 32;
+
+// hist[tile*E + e] = number of non-zero map entries of column e in the tile.
+__global__ __launch_bounds__(256) void mask_count_kernel(const uint8_t* __restrict__ map, int64_t T, int32_t E,
+                                                         uint32_t* __restrict__ hist) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    uint8_t m[kMaskTile];
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) m[i] = (t0 + i < T) ? map[(t0 + i) * E + e] : 0;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) c += m[i] != 0 ? 1u : 0u;
+    hist[static_cast<int64_t>(blockIdx.x) * E + e] = c;
   }
-  if (j < N && j >= static_cast<int64_t>(*total)) pp[j] = P(0);
+}
+
+// permute_probs[start[e] + off[tile*E + e] + running count] = probs[t, e]; entries at
+// positions >= N are dropped; positions from start[E] (the number of non-zero entries)
+// up to N get 0.
+template <typename P>
+__global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __restrict__ map,
+                                                           const P* __restrict__ probs, int64_t T, int32_t E,
+                                                           const uint32_t* __restrict__ off,
+                                                           const uint32_t* __restrict__ start,
+                                                           P* __restrict__ pp, int64_t N) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    uint32_t pos = start[e] + off[static_cast<int64_t>(blockIdx.x) * E + e];
+    uint8_t m[kMaskTile];
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) m[i] = (t0 + i < T) ? map[(t0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) {
+      if (m[i] != 0) {
+        if (pos < N) pp[pos] = probs[(t0 + i) * E + e];
+        ++pos;
+      }
+    }
+  }
+  const uint32_t filled = start[E];
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < N;
+       g += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    if (g >= filled) pp[g] = P(0);
 }
 
 // Padded inversion, single pass: out_index / permute_token_id at the sorted position, and
@@ -134,7 +219,8 @@ __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint32_t* __res
 template <typename P>
 __global__ __launch_bounds__(256) void padded_scatter_kernel(const int32_t* __restrict__ sI, int32_t T,
                                                              const uint32_t* __restrict__ packed,
-                                                             const uint32_t* __restrict__ off, int nt,
+                                                             const uint32_t* __restrict__ off,
+                                                             const uint32_t* __restrict__ start, int nb,
                                                              int tile_shift, int64_t n,
                                                              int32_t* __restrict__ out_index,
                                                              int32_t* __restrict__ token_out,
@@ -144,7 +230,7 @@ __global__ __launch_bounds__(256) void padded_scatter_kernel(const int32_t* __re
   if (j >= n) return;
   const int32_t v = sI[j];
   uint32_t pos, dig;
-  if (placed_position(packed, off, nt, tile_shift, j, pos, dig)) {
+  if (placed_position(packed, off, start, nb, tile_shift, j, pos, dig)) {
     out_index[pos] = static_cast<int32_t>(j);
     if (token_out != nullptr) token_out[pos] = v;
   }
@@ -184,15 +270,17 @@ static void launch_rank(const SortPass& p, KS ks, uint32_t* packed, uint32_t* hi
                        p.nbits, p.nb, packed, hist, p.nt, tile_err);
 }
 
-static void launch_scan(const SortPass& p, uint32_t* hist, uint32_t* total, uint32_t* bucket_start, hipStream_t s) {
+static void launch_scan(const SortPass& p, uint32_t* hist, uint32_t* start, uint32_t* total, hipStream_t s) {
   ScanTail none{nullptr, 0, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), 0, s, hist,
-                     static_cast<int64_t>(p.nb) * p.nt, total, bucket_start, p.nb, p.nt, none);
+  const size_t lds = static_cast<size_t>(p.nb) * sizeof(uint32_t);
+  allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), lds);
+  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), lds, s, hist, p.nb, p.nt, start, total, none);
 }
 
 struct SortBufs {
   uint32_t* packed;
   uint32_t* hist;
+  uint32_t* start;  // nb + 1 entries of the widest pass
   uint32_t* kA; uint32_t* vA; uint32_t* kB; uint32_t* vB;
 };
 
@@ -209,16 +297,16 @@ static void run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const SortBu
     const SortPass& p = sp.pass[i];
     if (i == 0) launch_rank(p, ks0, b.packed, b.hist, nullptr, s);
     else launch_rank(p, KeyArray{kin}, b.packed, b.hist, nullptr, s);
-    launch_scan(p, b.hist, nullptr, nullptr, s);
+    launch_scan(p, b.hist, b.start, nullptr, s);
     if (i == sp.npasses - 1) break;
     const unsigned g = grid_for(p.n, 256);
     if (i == 0)
       hipLaunchKernelGGL((lsd_scatter_kernel<KS, true, 0>), dim3(g), dim3(256), 0, s, ks0, vin, b.packed, b.hist,
-                         p.nt, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
+                         b.start, p.nb, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
                          static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr), 0);
     else
       hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 0>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                         b.packed, b.hist, p.nt, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
+                         b.packed, b.hist, b.start, p.nb, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
                          static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr), 0);
     kin = kout;
     vin = vout;
@@ -271,11 +359,9 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
     }
     if (p->K > 512) return FFNWB_ERR_INNER_NULLPTR;
     if (has_probs) {
-      const int64_t n0 = p->T * p->E;
-      p->mask_pass = make_pass(n0, static_cast<int>(p->E), bits_for(static_cast<uint64_t>(p->E - 1)), 0);
-      c.take<uint32_t>(n0);                                                   // packed
-      c.take<uint32_t>(static_cast<size_t>(p->E) * p->mask_pass.nt);          // histogram
-      c.take<uint32_t>(1);                                                    // compacted count
+      p->mask_tiles = (p->T + kMaskTile - 1) / kMaskTile;
+      c.take<uint32_t>(static_cast<size_t>(p->E) * p->mask_tiles);           // histogram
+      c.take<uint32_t>(static_cast<size_t>(p->E) + 1);                        // column starts
       if (d->permute_probs == nullptr) c.take<uint8_t>(static_cast<size_t>(p->N) * p->pelt);
     }
     p->need_aux = d->out_index != nullptr || d->permute_token_id != nullptr;
@@ -283,6 +369,7 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
       p->sort = make_sort_plan(p->N, static_cast<uint64_t>(p->rows) + 1);
       c.take<uint32_t>(p->N);
       c.take<uint32_t>(p->sort.hist_words);
+      c.take<uint32_t>(static_cast<size_t>(p->sort.max_nb) + 1);
       if (p->sort.npasses > 1)
         for (int i = 0; i < 4; ++i) c.take<uint32_t>(p->N);
     }
@@ -301,6 +388,7 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
     p->sort = make_sort_plan(p->N, static_cast<uint64_t>(p->T) + 1);
     c.take<uint32_t>(p->N);                                // packed
     c.take<uint32_t>(p->sort.hist_words);                  // histogram
+    c.take<uint32_t>(static_cast<size_t>(p->sort.max_nb) + 1);  // digit starts of a pass
     c.take<uint32_t>(static_cast<size_t>(p->T) + 2);       // token segments
     if (d->out_index == nullptr) c.take<int32_t>(p->N);    // sorted order for the reduce
     if (has_probs && d->permute_probs == nullptr) c.take<uint8_t>(static_cast<size_t>(p->N) * p->pelt);
@@ -311,44 +399,61 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
   return FFNWB_OK;
 }
 
-template <class TT, class TW, int MODE>
-static void launch_reduce_t(const ReduceArgs& ra, bool vec, int64_t T, int threads, hipStream_t s) {
-  if (T == 0) return;
-  if (vec)
-    hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, true>), dim3(static_cast<unsigned>(T)), dim3(threads),
-                       0, s, ra);
-  else
-    hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, false>), dim3(static_cast<unsigned>(T)),
-                       dim3(threads), 0, s, ra);
+// Reduce launch shape: `cpt` 16-byte chunks per thread (0 = element-wise kernel).
+struct ReduceShape {
+  int cpt = 1;
+  int threads = 64;
+};
+
+static ReduceShape reduce_shape(bool vec, int64_t H, int elt) {
+  ReduceShape r;
+  const int64_t work = vec ? (H * elt / 16) : H;
+  if (!vec) {
+    r.cpt = 0;
+  } else if (work <= 1024) {
+    r.cpt = 1;
+  } else if (work <= 2048) {
+    r.cpt = 2;
+  } else {
+    r.cpt = 4;
+  }
+  const int64_t per = r.cpt > 0 ? (work + r.cpt - 1) / r.cpt : work;
+  int64_t th = (per + 63) / 64 * 64;
+  if (th > 1024) th = 1024;
+  if (th < 64) th = 64;
+  r.threads = static_cast<int>(th);
+  return r;
 }
 
-template <class TT, class TW>
-static void launch_reduce_w(const ReduceArgs& ra, int mode, bool vec, int64_t T, int threads, hipStream_t s) {
-  switch (mode) {
-    case kNonPad: launch_reduce_t<TT, TW, kNonPad>(ra, vec, T, threads, s); break;
-    case kNonPadW2: launch_reduce_t<TT, TW, kNonPadW2>(ra, vec, T, threads, s); break;
-    case kNonPadW1: launch_reduce_t<TT, TW, kNonPadW1>(ra, vec, T, threads, s); break;
-    case kPad: launch_reduce_t<TT, TW, kPad>(ra, vec, T, threads, s); break;
-    default: launch_reduce_t<TT, TW, kPadW>(ra, vec, T, threads, s); break;
+template <class TT, class TW, int MODE>
+static void launch_reduce_t(const ReduceArgs& ra, const ReduceShape& sh, int64_t T, hipStream_t s) {
+  if (T == 0) return;
+  const dim3 grid(static_cast<unsigned>(T)), block(sh.threads);
+  switch (sh.cpt) {
+    case 0: hipLaunchKernelGGL((unpermute_reduce_elem_kernel<TT, TW, MODE>), grid, block, 0, s, ra); break;
+    case 1: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 1>), grid, block, 0, s, ra); break;
+    case 2: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 2>), grid, block, 0, s, ra); break;
+    default: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 4>), grid, block, 0, s, ra); break;
   }
 }
 
-static void launch_reduce(const ReduceArgs& ra, int dtype, int pdtype, int mode, bool vec, int64_t T, int threads,
-                          hipStream_t s) {
-  if (dtype == FFNWB_DT_FP16) launch_reduce_w<TF16, TF16>(ra, mode, vec, T, threads, s);
-  else if (dtype == FFNWB_DT_FP32) launch_reduce_w<TF32, TF32>(ra, mode, vec, T, threads, s);
-  else if (pdtype == FFNWB_DT_FP32) launch_reduce_w<TBF16, TF32>(ra, mode, vec, T, threads, s);
-  else launch_reduce_w<TBF16, TBF16>(ra, mode, vec, T, threads, s);
+template <class TT, class TW>
+static void launch_reduce_w(const ReduceArgs& ra, int mode, const ReduceShape& sh, int64_t T, hipStream_t s) {
+  switch (mode) {
+    case kNonPad: launch_reduce_t<TT, TW, kNonPad>(ra, sh, T, s); break;
+    case kNonPadW2: launch_reduce_t<TT, TW, kNonPadW2>(ra, sh, T, s); break;
+    case kNonPadW1: launch_reduce_t<TT, TW, kNonPadW1>(ra, sh, T, s); break;
+    case kPad: launch_reduce_t<TT, TW, kPad>(ra, sh, T, s); break;
+    default: launch_reduce_t<TT, TW, kPadW>(ra, sh, T, s); break;
+  }
 }
 
-template <typename P>
-static void launch_mask_scatter(const UnpermutePlan& p, const uint32_t* packed, const uint32_t* hist,
-                                const void* probs, void* pp, const uint32_t* total, hipStream_t s) {
-  const int64_t n0 = p.T * p.E;
-  const int64_t g = n0 > p.N ? n0 : p.N;
-  if (g == 0) return;
-  hipLaunchKernelGGL(mask_scatter_kernel<P>, dim3(grid_for(g, 256)), dim3(256), 0, s, packed, hist, p.mask_pass.nt,
-                     p.mask_pass.tile_shift, n0, static_cast<const P*>(probs), static_cast<P*>(pp), p.N, total);
+static void launch_reduce(const ReduceArgs& ra, int dtype, int pdtype, int mode, const ReduceShape& sh, int64_t T,
+                          hipStream_t s) {
+  if (dtype == FFNWB_DT_FP16) launch_reduce_w<TF16, TF16>(ra, mode, sh, T, s);
+  else if (dtype == FFNWB_DT_FP32) launch_reduce_w<TF32, TF32>(ra, mode, sh, T, s);
+  else if (pdtype == FFNWB_DT_FP32) launch_reduce_w<TBF16, TF32>(ra, mode, sh, T, s);
+  else launch_reduce_w<TBF16, TBF16>(ra, mode, sh, T, s);
 }
 
 int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* ws, hipStream_t s) {
@@ -358,9 +463,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
   void* pprobs = d->permute_probs;
   const bool vec = ((p.H * p.elt) % 16 == 0) &&
                    ((reinterpret_cast<uintptr_t>(d->permuted_tokens) | reinterpret_cast<uintptr_t>(d->unpermuted_tokens)) % 16 == 0);
-  const int64_t work = vec ? (p.H * p.elt / 16) : p.H;
-  int threads = static_cast<int>(((work < 1024 ? work : 1024) + 63) / 64 * 64);
-  if (threads < 64) threads = 64;
+  const ReduceShape shape = reduce_shape(vec, p.H, p.elt);
 
   ReduceArgs ra{};
   ra.x = static_cast<const uint8_t*>(d->permuted_tokens);
@@ -371,31 +474,40 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
 
   if (!p.padded) {
     if (p.has_probs) {
-      const int64_t n0 = p.T * p.E;
-      uint32_t* packed = c.take<uint32_t>(n0);
-      uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.E) * p.mask_pass.nt);
-      uint32_t* total = c.take<uint32_t>(1);
+      const int nt = static_cast<int>(p.mask_tiles);
+      uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.E) * nt);
+      uint32_t* cstart = c.take<uint32_t>(static_cast<size_t>(p.E) + 1);
       if (pprobs == nullptr) pprobs = c.take<uint8_t>(static_cast<size_t>(p.N) * p.pelt);
-      if (n0 > 0) {
-        launch_rank(p.mask_pass, KeyRoutingMap{d->routing_map, static_cast<int32_t>(p.E)}, packed, hist, nullptr, s);
-        launch_scan(p.mask_pass, hist, total, nullptr, s);
-      } else {
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, s, total, int64_t{1}, 0u);
+      const int th = static_cast<int>(p.E >= 256 ? 256 : (p.E + 63) / 64 * 64);
+      if (nt > 0) {
+        hipLaunchKernelGGL(mask_count_kernel, dim3(nt), dim3(th), 0, s, d->routing_map, p.T,
+                           static_cast<int32_t>(p.E), hist);
+        SortPass mp;
+        mp.nb = static_cast<int>(p.E);
+        mp.nt = nt;
+        launch_scan(mp, hist, cstart, nullptr, s);
+        if (p.pelt == 4)
+          hipLaunchKernelGGL(mask_scatter_kernel<uint32_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
+                             static_cast<const uint32_t*>(d->probs), p.T, static_cast<int32_t>(p.E), hist, cstart,
+                             static_cast<uint32_t*>(pprobs), p.N);
+        else
+          hipLaunchKernelGGL(mask_scatter_kernel<uint16_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
+                             static_cast<const uint16_t*>(d->probs), p.T, static_cast<int32_t>(p.E), hist, cstart,
+                             static_cast<uint16_t*>(pprobs), p.N);
       }
-      if (p.pelt == 4) launch_mask_scatter<uint32_t>(p, packed, hist, d->probs, pprobs, total, s);
-      else launch_mask_scatter<uint16_t>(p, packed, hist, d->probs, pprobs, total, s);
     }
     ra.sI = sI;
     ra.K = static_cast<int32_t>(p.K);
     ra.w = pprobs;
     const int mode = !p.has_probs ? kNonPad : (d->weight_index == 1 ? kNonPadW1 : kNonPadW2);
     if (!record_event(d->ev_reduce_begin, s)) return FFNWB_ERR_RUNTIME;
-    launch_reduce(ra, d->dtype, d->probs_dtype, mode, vec, p.T, threads, s);
+    launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s);
     if (!record_event(d->ev_reduce_end, s)) return FFNWB_ERR_RUNTIME;
     if (p.need_aux && p.N > 0) {
       SortBufs b{};
       b.packed = c.take<uint32_t>(p.N);
       b.hist = c.take<uint32_t>(p.sort.hist_words);
+      b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
       if (p.sort.npasses > 1) {
         b.kA = c.take<uint32_t>(p.N); b.vA = c.take<uint32_t>(p.N);
         b.kB = c.take<uint32_t>(p.N); b.vB = c.take<uint32_t>(p.N);
@@ -407,12 +519,14 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
       const unsigned g = grid_for(p.N, 256);
       if (p.sort.npasses == 1)
         hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, s, ks,
-                           static_cast<const uint32_t*>(nullptr), b.packed, b.hist, last.nt, last.tile_shift, p.N,
+                           static_cast<const uint32_t*>(nullptr), b.packed, b.hist, b.start, last.nb,
+                           last.tile_shift, p.N,
                            static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
                            d->permute_token_id, sI, static_cast<int32_t>(p.K));
       else
         hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                           b.packed, b.hist, last.nt, last.tile_shift, p.N, static_cast<uint32_t*>(nullptr),
+                           b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N,
+                           static_cast<uint32_t*>(nullptr),
                            static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
                            static_cast<int32_t>(p.K));
     }
@@ -420,6 +534,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     SortBufs b{};
     b.packed = c.take<uint32_t>(p.N);
     b.hist = c.take<uint32_t>(p.sort.hist_words);
+    b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
     uint32_t* seg = c.take<uint32_t>(static_cast<size_t>(p.T) + 2);
     int32_t* order = d->out_index ? d->out_index : c.take<int32_t>(p.N);
     if (p.has_probs && pprobs == nullptr) pprobs = c.take<uint8_t>(static_cast<size_t>(p.N) * p.pelt);
@@ -437,21 +552,22 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     } else if (p.sort.npasses == 1) {
       const SortPass& ps = p.sort.pass[0];
       launch_rank(ps, ks, b.packed, b.hist, nullptr, s);
-      launch_scan(ps, b.hist, nullptr, seg, s);
+      launch_scan(ps, b.hist, seg, nullptr, s);  // digit starts = token segments
       if (p.pelt == 4)
         hipLaunchKernelGGL(padded_scatter_kernel<uint32_t>, dim3(g), dim3(256), 0, s, sI, static_cast<int32_t>(p.T),
-                           b.packed, b.hist, ps.nt, ps.tile_shift, p.N, order, d->permute_token_id,
+                           b.packed, b.hist, seg, ps.nb, ps.tile_shift, p.N, order, d->permute_token_id,
                            static_cast<const uint32_t*>(d->probs), p.E, p.C, static_cast<uint32_t*>(pprobs));
       else
         hipLaunchKernelGGL(padded_scatter_kernel<uint16_t>, dim3(g), dim3(256), 0, s, sI, static_cast<int32_t>(p.T),
-                           b.packed, b.hist, ps.nt, ps.tile_shift, p.N, order, d->permute_token_id,
+                           b.packed, b.hist, seg, ps.nb, ps.tile_shift, p.N, order, d->permute_token_id,
                            static_cast<const uint16_t*>(d->probs), p.E, p.C, static_cast<uint16_t*>(pprobs));
     } else {
       const uint32_t *kin, *vin;
       run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, s);
       const SortPass& last = p.sort.pass[p.sort.npasses - 1];
       hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 2>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                         b.packed, b.hist, last.nt, last.tile_shift, p.N, skeys, static_cast<uint32_t*>(nullptr),
+                         b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N, skeys,
+                         static_cast<uint32_t*>(nullptr),
                          order, d->permute_token_id, sI, 0);
       hipLaunchKernelGGL(segment_bounds_kernel, dim3(grid_for(p.N + 1, 256)), dim3(256), 0, s, skeys, p.N,
                          static_cast<uint32_t>(p.T) + 1u, seg);
@@ -469,7 +585,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     ra.w = pprobs;
     const int mode = p.has_probs ? kPadW : kPad;
     if (!record_event(d->ev_reduce_begin, s)) return FFNWB_ERR_RUNTIME;
-    launch_reduce(ra, d->dtype, d->probs_dtype, mode, vec, p.T, threads, s);
+    launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s);
     if (!record_event(d->ev_reduce_end, s)) return FFNWB_ERR_RUNTIME;
   }
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
