@@ -42,14 +42,15 @@ struct BatchArgs {
 struct KeyBatching {
   BatchArgs a;
   __device__ uint32_t key(int64_t s, bool& valid, bool& err) const {
-    valid = false; err = false;
-    if (a.mask != nullptr && a.mask[s] != 0) return 0;
+    // every input of the slot is loaded before any decision, so the loads overlap
     const uint32_t c = static_cast<uint32_t>(s) / static_cast<uint32_t>(a.chunk);
+    const uint8_t m = a.mask != nullptr ? a.mask[s] : 0;
     const int32_t layer = (a.layer_ids != nullptr && a.layer_num >= 1) ? a.layer_ids[c] : 0;
     const int32_t e = a.expert_ids[s];
-    if (e < 0 || e >= a.per_layer || layer < 0 || layer >= a.L) { err = true; return 0; }
-    valid = true;
-    return static_cast<uint32_t>(layer * a.per_layer + e);
+    const bool ok = e >= 0 && e < a.per_layer && layer >= 0 && layer < a.L;
+    valid = m == 0 && ok;
+    err = m == 0 && !ok;
+    return valid ? static_cast<uint32_t>(layer * a.per_layer + e) : 0u;
   }
 };
 
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
                                                              int32_t* err_count) {
   constexpr int R = 4;
   extern __shared__ uint32_t lds_words[];
-  __shared__ uint32_t wsum[kRankThreads / kWave + 1];
+  __shared__ uint32_t wsum[kRankThreads / kWave + 1];  // block_exscan scratch
   __shared__ uint32_t err_w[kRankWaves];
   const int nbp = rank_lds_stride(nb);
   uint16_t* hist = reinterpret_cast<uint16_t*>(lds_words);
@@ -184,12 +185,12 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
+    const bool in = s < a.Y;
     bool v = false, e = false;
-    uint32_t key = 0;
-    if (s < a.Y) key = ks.key(s, v, e);
+    const uint32_t key = ks.key(in ? s : a.Y - 1, v, e);
     dig[r] = key;
-    val[r] = v;
-    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e)));
+    val[r] = v && in;
+    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e && in)));
   }
   rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
   if (lane == 0) err_w[w] = nerr;
@@ -424,7 +425,7 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   ScanTail tail{d->group_list, d->expert_num, d->actual_token_num, d->err_count, tile_err};
-  const size_t scan_lds = static_cast<size_t>(nb) * sizeof(uint32_t);
+  const size_t scan_lds = scan_lds_bytes(nb);
   allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), scan_lds);
   hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), scan_lds, s, hist, nb, p.pass.nt, kstart,
                      static_cast<uint32_t*>(nullptr), tail);

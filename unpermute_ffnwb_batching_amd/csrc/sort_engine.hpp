@@ -13,9 +13,9 @@
 // value plus the number of equal-digit lanes below it.  After a barrier, a per-digit
 // prefix over the 4 waves turns the per-wave counters into per-wave bases and gives the
 // tile's digit histogram, written tile-major (hist[tile*nb + digit], coalesced).
-// One workgroup then turns every digit's column of that matrix into an exclusive prefix
-// over tiles (in place) and scans the digit totals into start[digit].  Element j's output
-// position is start[digit] + hist[tile*nb + digit] + rank: ties keep input order.
+// One workgroup then turns each digit's column into a prefix over tiles (in place) and
+// scans the digit totals into start[digit]; element j's output position is
+// start[digit] + hist[tile*nb + digit] + rank: ties keep input order.
 #pragma once
 
 #include "device_common.hpp"
@@ -61,35 +61,60 @@ __device__ __forceinline__ void rank_rounds(const uint32_t (&dig)[R], const bool
   }
 }
 
-// Exclusive scan over a workgroup of NT threads.  `lds` holds NT/64 + 1 words.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* lds, uint32_t& total) {
-  constexpr int NW = NT / kWave;
-  const int lane = static_cast<int>(lane_id());
-  const int w = threadIdx.x / kWave;
-  uint32_t x = v;
+// Inclusive scan of one value per lane across the calling wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const uint32_t y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
-  if (lane == kWave - 1) lds[w] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < NW; ++i) { const uint32_t t = lds[i]; lds[i] = run; run += t; }
-    lds[NW] = run;
+  return x;
+}
+
+// K independent exclusive scans over a workgroup of NT threads, whose results are laid
+// end to end: the K sequences are concatenated in order (sequence 0 first), so v[k] of
+// thread i becomes the sum of all sequences before k plus sequence k's values of
+// threads before i.  `lds` holds K * NT/64 + 1 words; total = sum of everything.
+template <int NT, int K>
+__device__ __forceinline__ void block_exscan_multi(uint32_t (&v)[K], uint32_t* lds, uint32_t& total) {
+  constexpr int NW = NT / kWave;
+  static_assert(K * NW <= kWave, "wave totals must fit one wave");
+  const int lane = static_cast<int>(lane_id());
+  const int w = threadIdx.x / kWave;
+  uint32_t x[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] = wave_inclusive_scan(v[k], lane);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) lds[k * NW + w] = x[k];
   }
   __syncthreads();
-  total = lds[NW];
-  const uint32_t r = lds[w] + x - v;
+  if (w == 0) {
+    const uint32_t y = lane < K * NW ? lds[lane] : 0u;
+    const uint32_t inc = wave_inclusive_scan(y, lane);
+    if (lane < K * NW) lds[lane] = inc - y;
+    if (lane == kWave - 1) lds[K * NW] = inc;
+  }
   __syncthreads();
-  return r;
+  total = lds[K * NW];
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = lds[k * NW + w] + x[k] - v[k];
+  __syncthreads();
+}
+
+// Exclusive scan over a workgroup of NT threads.  `lds` holds NT/64 + 1 words.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* lds, uint32_t& total) {
+  uint32_t a[1] = {v};
+  block_exscan_multi<NT, 1>(a, lds, total);
+  return a[0];
 }
 
 // ------------------------------------------------------------------ key sources
 // Each returns the element's key and whether it takes part in the sort; `err` flags
-// elements dropped because of an out-of-range id (batching only).
+// elements dropped because of an out-of-range id (batching only).  Callers pass an
+// in-range index (clamped), and the sources load unconditionally, so that the loads of
+// all rounds of a tile are in flight together instead of one round at a time.
 
 // Padded unpermute: key = token id, entries outside [0, T) share the last bucket T.
 struct KeyPadded {
@@ -142,12 +167,12 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t j = base + r * kWave + lane;
+    const bool in = j < n;
     bool v = false, e = false;
-    uint32_t key = 0;
-    if (j < n) key = ks.key(j, v, e);
+    const uint32_t key = ks.key(in ? j : n - 1, v, e);
     dig[r] = (key >> shift) & dmask;
-    val[r] = v;
-    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e)));
+    val[r] = v && in;
+    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e && in)));
   }
   rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
   if (lane == 0) err_w[w] = nerr;
@@ -173,12 +198,15 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
 }
 
 // ------------------------------------------------------------------ scan of the histogram
-// One 1024-thread workgroup.  Phase 1: thread k walks digit k's column of the tile-major
-// histogram (coalesced across threads), replacing each count by the number of elements
-// with that digit in earlier tiles, and keeps the digit's total in LDS.  Phase 2: an
-// exclusive scan of the totals gives start[k] (start[nb] = n placed).  Optional tail for
-// batching: compact group_list rows {k, count_k} for count_k > 0 then {0,0},
-// actual_token_num and err_count = sum of tile_err[0..nt).
+// One 1024-thread workgroup turns the tile-major histogram into per-digit prefixes over
+// tiles, in place (h[t*nb + k] = elements of digit k in tiles before t), and writes
+// start[k] = elements with a smaller digit (start[nb] = total).  Digit k's column is
+// walked by consecutive threads for consecutive k (coalesced); when there are fewer
+// digits than threads, each column is split into G tile segments walked in parallel and
+// joined through LDS; when there are more, each thread walks several columns with their
+// loads interleaved.  Column totals are kept in LDS and scanned in digit order.
+// Optional tail for batching: compact group_list rows {k, count_k} for count_k > 0 then
+// {0,0}, actual_token_num and err_count = sum of tile_err[0..nt).
 struct ScanTail {
   int64_t* group_list;    // nullptr = no batching tail
   int64_t group_rows;
@@ -187,38 +215,89 @@ struct ScanTail {
   const uint32_t* tile_err;
 };
 
-constexpr int kScanMaxBuckets = 20480;  // LDS holds every digit total (80 KiB)
+constexpr int kScanMaxBuckets = 20480;  // digit totals in LDS: 80 KiB
+
+// Sums (or, with `write`, overwrites with running prefixes starting at `base`) the cells
+// h[t*nb + k] for t in [t0, t1), 16 loads in flight at a time.
+__device__ __forceinline__ uint32_t walk_column(uint32_t* __restrict__ h, int nb, int k, int t0, int t1,
+                                                bool write, uint32_t base) {
+  constexpr int B = 16;
+  uint32_t run = base;
+  for (int t = t0; t < t1; t += B) {
+    uint32_t c[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) c[u] = h[static_cast<int64_t>(min(t + u, t1 - 1)) * nb + k];  // clamped
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (t + u < t1) {
+        if (write) h[static_cast<int64_t>(t + u) * nb + k] = run;
+        run += c[u];
+      }
+    }
+  }
+  return run;
+}
 
 static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t* __restrict__ h, int nb, int nt,
                                                                         uint32_t* __restrict__ start,
                                                                         uint32_t* __restrict__ total_out,
                                                                         ScanTail tail) {
-  extern __shared__ uint32_t tot[];  // [nb]
+  extern __shared__ uint32_t tot[];  // [nb] digit totals, then [G][KW] segment sums
   __shared__ uint32_t wsum[kScanThreads / kWave + 1];
-  for (int k = threadIdx.x; k < nb; k += kScanThreads) {
-    uint32_t run = 0;
-    int t = 0;
-    for (; t + 8 <= nt; t += 8) {
-      uint32_t c[8];
+  const int tid = threadIdx.x;
+  if (nb * 2 <= kScanThreads && nt >= 256) {
+    // few digits, long columns: G segments per column
+    const int KW = (nb + kWave - 1) / kWave * kWave;
+    const int G = kScanThreads / KW;
+    const int kk = tid % KW, g = tid / KW;
+    const int S = (nt + G - 1) / G;
+    const int t0 = min(nt, g * S), t1 = min(nt, t0 + S);
+    uint32_t* seg = tot + nb;
+    const bool act = g < G && kk < nb;
+    const uint32_t sum = act ? walk_column(h, nb, kk, t0, t1, false, 0) : 0u;
+    if (g < G) seg[g * KW + kk] = sum;
+    __syncthreads();
+    if (act) {
+      uint32_t base = 0;
+      for (int gg = 0; gg < g; ++gg) base += seg[gg * KW + kk];
+      walk_column(h, nb, kk, t0, t1, true, base);
+      if (g == G - 1) tot[kk] = base + sum;
+    }
+  } else {
+    // thread walks columns k = tid, tid + 1024, ...; up to 4 columns interleaved when short
+    const int per = (nt <= 8) ? 4 : 1;
+    for (int k0 = tid; k0 < nb; k0 += kScanThreads * per) {
+      if (per == 4 && nt <= 8) {
+        uint32_t c[4][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = h[static_cast<int64_t>(t + u) * nb + k];
+        for (int i = 0; i < 4; ++i) {
+          const int k = min(k0 + i * kScanThreads, nb - 1);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        h[static_cast<int64_t>(t + u) * nb + k] = run;
-        run += c[u];
+          for (int u = 0; u < 8; ++u) c[i][u] = h[static_cast<int64_t>(min(u, nt - 1)) * nb + k];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = k0 + i * kScanThreads;
+          if (k >= nb) continue;
+          uint32_t run = 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (u < nt) {
+              h[static_cast<int64_t>(u) * nb + k] = run;
+              run += c[i][u];
+            }
+          }
+          tot[k] = run;
+        }
+      } else {
+        tot[k0] = walk_column(h, nb, k0, 0, nt, true, 0);
       }
     }
-    for (; t < nt; ++t) {
-      const uint32_t c = h[static_cast<int64_t>(t) * nb + k];
-      h[static_cast<int64_t>(t) * nb + k] = run;
-      run += c;
-    }
-    tot[k] = run;
   }
   __syncthreads();
   // exclusive scan of tot[0..nb): thread i owns the contiguous run [i*per, (i+1)*per)
   const int per = (nb + kScanThreads - 1) / kScanThreads;
-  const int lo = min(nb, static_cast<int>(threadIdx.x) * per);
+  const int lo = min(nb, tid * per);
   const int hi = min(nb, lo + per);
   uint32_t sum = 0;
   for (int k = lo; k < hi; ++k) sum += tot[k];
@@ -228,7 +307,7 @@ static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t
     start[k] = pre;
     pre += tot[k];
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     start[nb] = total;
     if (total_out != nullptr) *total_out = total;
   }
@@ -236,7 +315,7 @@ static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t
   __syncthreads();
   uint32_t carry = 0;
   for (int k0 = 0; k0 < nb; k0 += kScanThreads) {
-    const int k = k0 + threadIdx.x;
+    const int k = k0 + tid;
     const uint32_t cnt = (k < nb) ? tot[k] : 0u;
     uint32_t present;
     const uint32_t slot = carry + block_exscan<kScanThreads>(cnt > 0 ? 1u : 0u, wsum, present);
@@ -246,18 +325,23 @@ static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t
     }
     carry += present;
   }
-  for (int64_t g = carry + threadIdx.x; g < tail.group_rows; g += kScanThreads) {
-    tail.group_list[2 * g] = 0;
-    tail.group_list[2 * g + 1] = 0;
+  for (int64_t gi = carry + tid; gi < tail.group_rows; gi += kScanThreads) {
+    tail.group_list[2 * gi] = 0;
+    tail.group_list[2 * gi + 1] = 0;
   }
   uint32_t e = 0;
-  for (int t = threadIdx.x; t < nt; t += kScanThreads) e += tail.tile_err[t];
+  for (int t = tid; t < nt; t += kScanThreads) e += tail.tile_err[t];
   uint32_t etot;
   (void)block_exscan<kScanThreads>(e, wsum, etot);
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     *tail.actual_token_num = static_cast<int64_t>(total);
     if (tail.err_count != nullptr) *tail.err_count = static_cast<int32_t>(etot);
   }
+}
+
+// Dynamic LDS of scan_hist_kernel for nb digits.
+__host__ __device__ inline size_t scan_lds_bytes(int nb) {
+  return (static_cast<size_t>(nb) + kScanThreads) * sizeof(uint32_t);
 }
 
 // Output position of element j after a ranking pass and the scan (false if not placed).

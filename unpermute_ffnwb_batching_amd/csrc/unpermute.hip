@@ -177,10 +177,10 @@ __global__ __launch_bounds__(256) void mask_count_kernel(const uint8_t* __restri
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     uint8_t m[kMaskTile];
 #pragma unroll
-    for (int i = 0; i < kMaskTile; ++i) m[i] = (t0 + i < T) ? map[(t0 + i) * E + e] : 0;
+    for (int i = 0; i < kMaskTile; ++i) m[i] = map[(t0 + i < T ? t0 + i : T - 1) * E + e];  // clamped: no branch
     uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < kMaskTile; ++i) c += m[i] != 0 ? 1u : 0u;
+    for (int i = 0; i < kMaskTile; ++i) c += (t0 + i < T && m[i] != 0) ? 1u : 0u;
     hist[static_cast<int64_t>(blockIdx.x) * E + e] = c;
   }
 }
@@ -197,13 +197,20 @@ __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __rest
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     uint32_t pos = start[e] + off[static_cast<int64_t>(blockIdx.x) * E + e];
+    // map bytes and probs of the whole tile column are loaded first (clamped rows, no
+    // branch), so the loads are in flight together; probs reads are coalesced across e
     uint8_t m[kMaskTile];
-#pragma unroll
-    for (int i = 0; i < kMaskTile; ++i) m[i] = (t0 + i < T) ? map[(t0 + i) * E + e] : 0;
+    P v[kMaskTile];
 #pragma unroll
     for (int i = 0; i < kMaskTile; ++i) {
-      if (m[i] != 0) {
-        if (pos < N) pp[pos] = probs[(t0 + i) * E + e];
+      const int64_t row = (t0 + i < T ? t0 + i : T - 1) * E + e;
+      m[i] = map[row];
+      v[i] = probs[row];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) {
+      if (t0 + i < T && m[i] != 0) {
+        if (pos < N) pp[pos] = v[i];
         ++pos;
       }
     }
@@ -272,7 +279,7 @@ static void launch_rank(const SortPass& p, KS ks, uint32_t* packed, uint32_t* hi
 
 static void launch_scan(const SortPass& p, uint32_t* hist, uint32_t* start, uint32_t* total, hipStream_t s) {
   ScanTail none{nullptr, 0, nullptr, nullptr, nullptr};
-  const size_t lds = static_cast<size_t>(p.nb) * sizeof(uint32_t);
+  const size_t lds = scan_lds_bytes(p.nb);
   allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), lds);
   hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), lds, s, hist, p.nb, p.nt, start, total, none);
 }
