@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--detail-iters", type=int, default=20, help="per-workload timed iterations (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of workloads to keep (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -173,11 +175,9 @@ def main():
     stream = torch.cuda.current_stream()
     K, W = args.steps, args.warmup
     have_np = "unpermute_nonpadded" in calls
-    hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for b, e in hot:  # torch creates the HIP event on its first record; the library records it again
-        b.record(stream)
-        e.record(stream)
-    torch.cuda.synchronize()
+    from unpermute_ffnwb_batching_amd.hip_events import HipEvent
+    # fence-free HIP events, recorded by the library around the gather-reduce kernel
+    hot = [(HipEvent(), HipEvent()) for _ in range(K)]
 
     def step(i=None):
         for n, call in calls.items():
@@ -191,6 +191,15 @@ def main():
     for _ in range(W):
         step()
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the scale
+        # that converts the counters of the library's kernels into bytes
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(K):
@@ -198,8 +207,16 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    hot_ms = float(np.mean([b.elapsed_time(e) for b, e in hot])) if have_np else None
+    hot_ms = float(np.mean([b.elapsed_ms(e) for b, e in hot])) if have_np else None
     print(f"# {K} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    # the same steps without the timing hooks, for reference
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record(stream)
+    for _ in range(K):
+        step()
+    e2.record(stream)
+    torch.cuda.synchronize()
+    ms_nohook = s2.elapsed_time(e2) / K
 
     # per-workload timing with L2 / Infinity Cache flushed before every iteration
     detail = {}
@@ -263,7 +280,8 @@ def main():
     value = step_bytes / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms, 4), "ms_per_step_without_timing_hooks": round(ms_nohook, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "moe_reorder_suite: " + "+".join(names),
                    "step_alg_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),

@@ -92,6 +92,15 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _event_handle(ev):
+    """hipEvent_t of a HipEvent (``.handle``) or of a torch.cuda.Event (``.cuda_event``)."""
+    if ev is None:
+        return None
+    if hasattr(ev, "handle"):
+        return ev.handle
+    return ctypes.c_void_p(ev.cuda_event)
+
+
 def _stream_handle(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -178,8 +187,8 @@ class BatchingCall:
         d.actual_token_num = _ptr(out["actual_token_num"])
         d.err_count = _ptr(out.get("err_count"))
         if ev_gather is not None:
-            d.ev_gather_begin = ctypes.c_void_p(ev_gather[0].cuda_event)
-            d.ev_gather_end = ctypes.c_void_p(ev_gather[1].cuda_event)
+            d.ev_gather_begin = _event_handle(ev_gather[0])
+            d.ev_gather_end = _event_handle(ev_gather[1])
         self.desc = d
         self.ws_bytes = ffnwb_batching_workspace_size(d)
         if workspace is None and self.ws_bytes:
@@ -187,8 +196,8 @@ class BatchingCall:
         self.workspace = workspace
 
     def set_gather_events(self, begin, end):
-        self.desc.ev_gather_begin = None if begin is None else ctypes.c_void_p(begin.cuda_event)
-        self.desc.ev_gather_end = None if end is None else ctypes.c_void_p(end.cuda_event)
+        self.desc.ev_gather_begin = _event_handle(begin)
+        self.desc.ev_gather_end = _event_handle(end)
 
     def run(self, stream=None):
         ws = self.workspace
@@ -264,8 +273,8 @@ class UnpermuteCall:
         d.permute_token_id = _ptr(out.get("permute_token_id"))
         d.permute_probs = _ptr(out.get("permute_probs"))
         if ev_reduce is not None:
-            d.ev_reduce_begin = ctypes.c_void_p(ev_reduce[0].cuda_event)
-            d.ev_reduce_end = ctypes.c_void_p(ev_reduce[1].cuda_event)
+            d.ev_reduce_begin = _event_handle(ev_reduce[0])
+            d.ev_reduce_end = _event_handle(ev_reduce[1])
         self.desc = d
         self.ws_bytes = moe_unpermute_workspace_size(d)
         if workspace is None and self.ws_bytes:
@@ -273,8 +282,8 @@ class UnpermuteCall:
         self.workspace = workspace
 
     def set_reduce_events(self, begin, end):
-        self.desc.ev_reduce_begin = None if begin is None else ctypes.c_void_p(begin.cuda_event)
-        self.desc.ev_reduce_end = None if end is None else ctypes.c_void_p(end.cuda_event)
+        self.desc.ev_reduce_begin = _event_handle(begin)
+        self.desc.ev_reduce_end = _event_handle(end)
 
     def run(self, stream=None):
         st = lib().moe_unpermute(ctypes.byref(self.desc), _ptr(self.workspace), ctypes.c_size_t(self.ws_bytes),
