@@ -112,3 +112,21 @@ def test_deterministic_repeat():
     for k in a:
         assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
     check_unpermute(case, b)
+
+
+def test_nondefault_streams_and_back_to_back_calls():
+    # the auxiliary order runs on a library side stream joined back to the caller's stream;
+    # check results on two user streams with calls in flight together
+    cases = [synth.unpermute_nonpadded_case(40 + i, T=500, K=4, E=32, H=256, dtype=synth.BF16,
+                                            probs_dtype=synth.FP32, n_empty=150) for i in range(2)]
+    refs = [oracle_unpermute(c) for c in cases]
+    calls = [prepare_unpermute(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for call, st in zip(calls, streams):
+            with torch.cuda.stream(st):
+                call.run(st)
+    torch.cuda.synchronize()
+    for c, call, ref in zip(cases, calls, refs):
+        check_unpermute(c, fetch_unpermute(call, c), ref)

@@ -16,6 +16,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -324,6 +325,42 @@ static void run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const SortBu
   *vals_in = vin;
 }
 
+// A library-owned stream per device on which the non-padded auxiliary sort runs, forked
+// from and joined back to the caller's stream with events, so that it overlaps the probs
+// compaction and the gather-reduce (it depends only on sortedIndices).  Created on first
+// use at the default priority; the mutex keeps each fork's record/wait pair together.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+static std::mutex g_side_mu;
+static SideStream g_side[kMaxDevices];
+
+static SideStream* side_stream_for(hipStream_t caller) {
+  int dev = 0;
+  if (caller != nullptr) dev = hipGetStreamDeviceId(caller);
+  else if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr && !ss.failed) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    const bool switch_dev = cur != dev;
+    if (switch_dev) (void)hipSetDevice(dev);
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      ss.stream = nullptr;
+    }
+    if (switch_dev) (void)hipSetDevice(cur);
+  }
+  return ss.failed ? nullptr : &ss;
+}
+
 int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
   if (d == nullptr || p == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
   if (d->permuted_tokens == nullptr || d->sorted_indices == nullptr || d->unpermuted_tokens == nullptr)
@@ -480,28 +517,74 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
   ra.out = static_cast<uint8_t*>(d->unpermuted_tokens);
 
   if (!p.padded) {
+    // workspace regions, in the order plan_unpermute sized them
+    const int nt = static_cast<int>(p.mask_tiles);
+    uint32_t* mhist = nullptr;
+    uint32_t* cstart = nullptr;
     if (p.has_probs) {
-      const int nt = static_cast<int>(p.mask_tiles);
-      uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.E) * nt);
-      uint32_t* cstart = c.take<uint32_t>(static_cast<size_t>(p.E) + 1);
+      mhist = c.take<uint32_t>(static_cast<size_t>(p.E) * nt);
+      cstart = c.take<uint32_t>(static_cast<size_t>(p.E) + 1);
       if (pprobs == nullptr) pprobs = c.take<uint8_t>(static_cast<size_t>(p.N) * p.pelt);
-      const int th = static_cast<int>(p.E >= 256 ? 256 : (p.E + 63) / 64 * 64);
-      if (nt > 0) {
-        hipLaunchKernelGGL(mask_count_kernel, dim3(nt), dim3(th), 0, s, d->routing_map, p.T,
-                           static_cast<int32_t>(p.E), hist);
-        SortPass mp;
-        mp.nb = static_cast<int>(p.E);
-        mp.nt = nt;
-        launch_scan(mp, hist, cstart, nullptr, s);
-        if (p.pelt == 4)
-          hipLaunchKernelGGL(mask_scatter_kernel<uint32_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
-                             static_cast<const uint32_t*>(d->probs), p.T, static_cast<int32_t>(p.E), hist, cstart,
-                             static_cast<uint32_t*>(pprobs), p.N);
-        else
-          hipLaunchKernelGGL(mask_scatter_kernel<uint16_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
-                             static_cast<const uint16_t*>(d->probs), p.T, static_cast<int32_t>(p.E), hist, cstart,
-                             static_cast<uint16_t*>(pprobs), p.N);
+    }
+    SortBufs b{};
+    const bool aux = p.need_aux && p.N > 0;
+    if (aux) {
+      b.packed = c.take<uint32_t>(p.N);
+      b.hist = c.take<uint32_t>(p.sort.hist_words);
+      b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
+      if (p.sort.npasses > 1) {
+        b.kA = c.take<uint32_t>(p.N); b.vA = c.take<uint32_t>(p.N);
+        b.kB = c.take<uint32_t>(p.N); b.vB = c.take<uint32_t>(p.N);
       }
+    }
+    // auxiliary order (out_index / permute_token_id) on the side stream
+    SideStream* side = nullptr;
+    if (aux) {
+      std::lock_guard<std::mutex> lock(g_side_mu);
+      side = side_stream_for(s);
+      hipStream_t as = s;
+      if (side != nullptr && hipEventRecord(side->fork, s) == hipSuccess &&
+          hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess) {
+        as = side->stream;
+      } else {
+        side = nullptr;
+      }
+      KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
+      const uint32_t *kin, *vin;
+      run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, as);
+      const SortPass& last = p.sort.pass[p.sort.npasses - 1];
+      const unsigned g = grid_for(p.N, 256);
+      if (p.sort.npasses == 1)
+        hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, as, ks,
+                           static_cast<const uint32_t*>(nullptr), b.packed, b.hist, b.start, last.nb,
+                           last.tile_shift, p.N,
+                           static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
+                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
+      else
+        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, as, KeyArray{kin}, vin,
+                           b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N,
+                           static_cast<uint32_t*>(nullptr),
+                           static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
+                           static_cast<int32_t>(p.K));
+      if (side != nullptr && hipEventRecord(side->join, side->stream) != hipSuccess) return FFNWB_ERR_RUNTIME;
+    }
+    // probs compaction, then the gather-reduce, on the caller's stream
+    if (p.has_probs && nt > 0) {
+      const int th = static_cast<int>(p.E >= 256 ? 256 : (p.E + 63) / 64 * 64);
+      hipLaunchKernelGGL(mask_count_kernel, dim3(nt), dim3(th), 0, s, d->routing_map, p.T,
+                         static_cast<int32_t>(p.E), mhist);
+      SortPass mp;
+      mp.nb = static_cast<int>(p.E);
+      mp.nt = nt;
+      launch_scan(mp, mhist, cstart, nullptr, s);
+      if (p.pelt == 4)
+        hipLaunchKernelGGL(mask_scatter_kernel<uint32_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
+                           static_cast<const uint32_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mhist, cstart,
+                           static_cast<uint32_t*>(pprobs), p.N);
+      else
+        hipLaunchKernelGGL(mask_scatter_kernel<uint16_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
+                           static_cast<const uint16_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mhist, cstart,
+                           static_cast<uint16_t*>(pprobs), p.N);
     }
     ra.sI = sI;
     ra.K = static_cast<int32_t>(p.K);
@@ -510,33 +593,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     if (!record_event(d->ev_reduce_begin, s)) return FFNWB_ERR_RUNTIME;
     launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s);
     if (!record_event(d->ev_reduce_end, s)) return FFNWB_ERR_RUNTIME;
-    if (p.need_aux && p.N > 0) {
-      SortBufs b{};
-      b.packed = c.take<uint32_t>(p.N);
-      b.hist = c.take<uint32_t>(p.sort.hist_words);
-      b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
-      if (p.sort.npasses > 1) {
-        b.kA = c.take<uint32_t>(p.N); b.vA = c.take<uint32_t>(p.N);
-        b.kB = c.take<uint32_t>(p.N); b.vB = c.take<uint32_t>(p.N);
-      }
-      KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
-      const uint32_t *kin, *vin;
-      run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, s);
-      const SortPass& last = p.sort.pass[p.sort.npasses - 1];
-      const unsigned g = grid_for(p.N, 256);
-      if (p.sort.npasses == 1)
-        hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, s, ks,
-                           static_cast<const uint32_t*>(nullptr), b.packed, b.hist, b.start, last.nb,
-                           last.tile_shift, p.N,
-                           static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
-                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
-      else
-        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                           b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N,
-                           static_cast<uint32_t*>(nullptr),
-                           static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
-                           static_cast<int32_t>(p.K));
-    }
+    if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
   } else {
     SortBufs b{};
     b.packed = c.take<uint32_t>(p.N);
