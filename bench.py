@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s (and % of peak) for batching and unpermute; rows/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "unpermute_reduce_nonpadded_bf16_T16384_topk8_H4096.traffic.txt")
-REDUCE_SOURCES = ["unpermute_ffnwb_batching_amd/csrc/unpermute.hip",
+REDUCE_SOURCES = ["unpermute_ffnwb_batching_amd/csrc/reduce_kernels.hpp",
                   "unpermute_ffnwb_batching_amd/csrc/device_common.hpp"]
 
 

@@ -29,6 +29,7 @@ RANDOM = [
     (6, 8, 8, 256, 8192, 8, synth.BF16, 10, 0, False, 0, False),       # max experts
     (2, 100, 64, 16, 5000, 1, synth.FP16, 999, 30, False, 0, False),   # K+1 = 64, 5000 keys
     (1024, 2, 1, 8, 16, 1, synth.FP16, 0, 0, True, 0, False),          # A = 1024 chunks
+    (64, 512, 9, 16, 256, 2, synth.FP16, 1000, 10, True, 0, False),    # Y = 294912: multi-launch sort
 ]
 
 
@@ -46,6 +47,15 @@ def test_random_shapes(params):
 def test_zipf_skew_and_layer_gaps():
     case = synth.batching_case(77, 32, 32, 9, 128, 512, 8, synth.BF16, n_masked=500,
                                expert_dist="zipf", zipf_s=1.6, layer_of_chunk="mod")
+    check_batching(case, run_batching(case))
+
+
+@pytest.mark.parametrize("A", [8, 32])
+def test_one_expert_takes_every_slot(A):
+    # one key holds nearly every slot (A = 8: one-launch order, A = 32: multi-launch sort)
+    case = synth.batching_case(78, A, 64, 9, 256, 64, 1, synth.BF16, n_masked=100)
+    case["expert_ids"][:] = 9
+    case["expert_ids"][::97] = 3
     check_batching(case, run_batching(case))
 
 

@@ -50,7 +50,9 @@ PAD = [
     (16, 64, 50, 128, synth.BF16, synth.FP32, 2, True, 0),     # capacity > tokens (with replacement)
     (4, 33, 200, 21, synth.BF16, synth.BF16, 1, True, 7),     # odd H
     (6, 10, 30, 64, synth.FP16, None, 0, False, 3),           # branch 3, no probs
-    (4, 8, 25000, 32, synth.FP32, synth.FP32, 2, True, 2),    # token count needs LSD passes
+    (4, 8, 25000, 32, synth.FP32, synth.FP32, 2, True, 2),    # 25001 keys, 32 entries
+    (64, 4500, 20000, 8, synth.FP16, synth.FP16, 4, True, 10),  # 288000 entries: multi-launch sort, one pass
+    (64, 4500, 30000, 8, synth.FP32, synth.FP32, 4, True, 10),  # 288000 entries, 30001 keys: LSD passes
 ]
 
 
@@ -60,6 +62,17 @@ def test_padded_random(params):
     case = synth.unpermute_padded_case(900 + E + C, E=E, C=C, T=T, H=H, dtype=dt, probs_dtype=pdt, topk=topk,
                                        with_probs=wp, n_invalid=inv)
     print(f"unpermute padded {params}", flush=True)
+    check_unpermute(case, run_unpermute(case))
+
+
+def test_padded_skewed_tokens():
+    # two tokens hold every capacity entry: one ordering workgroup owns them all and its
+    # waves read their slices again instead of keeping per-wave lists
+    case = synth.unpermute_padded_case(36, E=16, C=2048, T=4096, H=64, dtype=synth.BF16, probs_dtype=synth.FP32)
+    rng = np.random.default_rng(36)
+    case["sorted_indices"] = rng.choice(np.array([5, 6], np.int32), size=case["sorted_indices"].shape[0])
+    case["sorted_indices"][:7] = -1
+    print("unpermute padded skewed", flush=True)
     check_unpermute(case, run_unpermute(case))
 
 

@@ -12,9 +12,12 @@
 #include <stdio.h>
 
 #include "internal.hpp"
+#include "range_order.hpp"
 #include "sort_engine.hpp"
 
 namespace ffnwb {
+
+constexpr int64_t kBatchingRangeMaxSlots = 8192;
 
 struct BatchArgs {
   int64_t Y, chunk;
@@ -51,6 +54,62 @@ struct KeyBatching {
     valid = m == 0 && ok;
     err = m == 0 && !ok;
     return valid ? static_cast<uint32_t>(layer * a.per_layer + e) : 0u;
+  }
+};
+
+// The slot keys of 4 consecutive slots j0..j0+3 (j0 a multiple of 4) for the
+// range-partitioned order: one 16-byte load of expert ids and one 4-byte load of mask
+// bytes where aligned, and at most two layer lookups (4 consecutive slots cross at most
+// one chunk boundary when chunks hold at least 4 slots).  Same keys as KeyBatching.
+struct RoKeysBatching {
+  BatchArgs a;
+  __device__ __forceinline__ void key4(uint32_t j0, uint32_t (&k)[kRoVec], bool (&v)[kRoVec],
+                                       bool (&er)[kRoVec]) const {
+    const uint32_t Y = static_cast<uint32_t>(a.Y);
+    const bool full = j0 + kRoVec <= Y;
+    int32_t ex[kRoVec];
+    if (full && (reinterpret_cast<uintptr_t>(a.expert_ids) & 15) == 0) {
+      const int4 q = *reinterpret_cast<const int4*>(a.expert_ids + j0);
+      ex[0] = q.x; ex[1] = q.y; ex[2] = q.z; ex[3] = q.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRoVec; ++i) ex[i] = a.expert_ids[min(j0 + i, Y - 1)];
+    }
+    uint32_t m[kRoVec] = {0u, 0u, 0u, 0u};
+    if (a.mask != nullptr) {
+      if (full && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(a.mask + j0);
+#pragma unroll
+        for (int i = 0; i < kRoVec; ++i) m[i] = (q >> (8 * i)) & 0xffu;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRoVec; ++i) m[i] = a.mask[min(j0 + i, Y - 1)];
+      }
+    }
+    int32_t layer[kRoVec] = {0, 0, 0, 0};
+    if (a.layer_ids != nullptr && a.layer_num >= 1) {
+      const uint32_t chunk = static_cast<uint32_t>(a.chunk);
+      if (chunk >= kRoVec) {
+        const uint32_t jc = min(j0, Y - 1);
+        const uint32_t c0 = jc / chunk;
+        const uint32_t last = Y / chunk - 1u;  // last chunk
+        const uint32_t next = (c0 + 1u) * chunk;  // first slot of chunk c0 + 1 (<= Y < 2^31)
+        const int32_t l0 = a.layer_ids[c0];
+        const int32_t l1 = a.layer_ids[min(c0 + 1u, last)];
+#pragma unroll
+        for (int i = 0; i < kRoVec; ++i) layer[i] = (j0 + i < next) ? l0 : l1;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRoVec; ++i) layer[i] = a.layer_ids[min(j0 + i, Y - 1) / chunk];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRoVec; ++i) {
+      const bool ok = ex[i] >= 0 && ex[i] < a.per_layer && layer[i] >= 0 && layer[i] < a.L;
+      v[i] = m[i] == 0 && ok;
+      er[i] = m[i] == 0 && !ok;
+      k[i] = v[i] ? static_cast<uint32_t>(layer[i] * a.per_layer + ex[i]) : 0u;
+    }
   }
 };
 
@@ -129,17 +188,14 @@ __device__ __forceinline__ void write_row_ids(const BatchArgs& a, int64_t s, uin
 }
 
 // One wavefront per source slot (4 slots per workgroup).  The slot's output row is
-// start[key] + off[tile*nb + key] + rank; its group's first row is start[key].  The first
-// piece of the source row is loaded before that lookup, so the lookup's latency hides
-// under the row loads.
+// start[key] + (its tile's base for key) + rank; its group's first row is start[key].
+// The first piece of the source row is loaded before that lookup, so the lookup's
+// latency hides under the row loads.
 template <int VEC>
-__global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, const uint32_t* __restrict__ packed,
-                                                              const uint32_t* __restrict__ off,
-                                                              const uint32_t* __restrict__ start, int nb,
-                                                              int tile_shift) {
+__global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, Placement pl) {
   const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
   if (s >= a.Y) return;
-  const uint32_t p = uniform(packed[s]);
+  const uint32_t p = uniform(pl.packed[s]);
   if (p == kNoRank) return;
   const uint32_t lane = lane_id();
   const uint8_t* src = a.token_data + s * a.stride;
@@ -147,8 +203,8 @@ __global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, const
   RowPiece<VEC> first;
   if (VEC != 1) first.load(src, n16, 0, lane);
   const uint32_t key = p >> 16;
-  const uint32_t gstart = uniform(start[key]);
-  const uint32_t pos = gstart + uniform(off[(s >> tile_shift) * nb + key]) + (p & 0xffffu);
+  const uint32_t gstart = uniform(pl.start[key]);
+  const uint32_t pos = gstart + uniform(pl.tile_base(s >> pl.tile_shift, key)) + (p & 0xffffu);
   uint8_t* dst = a.y + static_cast<int64_t>(pos) * a.row_bytes;
   if (VEC != 1) {
     first.store(dst, n16, 0, lane);
@@ -157,6 +213,108 @@ __global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, const
     copy_row_rest<VEC>(src, dst, a.row_bytes, 0, lane);
   }
   if (lane == 0) write_row_ids(a, s, pos, gstart);
+}
+
+// Slot order in one launch (range-partitioned, see range_order.hpp).  Workgroup b owns
+// the keys [lo, lo + kr): for its slots it writes the output row pos_of[s] and the row
+// IDs (token id, offset in the group, session, micro-batch; the per-chunk ids are staged
+// in LDS so that placing a slot issues stores only), and for its non-empty keys their
+// group_list rows.  A key's group_list row is the number of
+// non-empty keys below it, which every workgroup finds from a presence array of the keys
+// below lo (filled with relaxed stores of 1: no read-modify-write).  Workgroup 0 also
+// marks the slots that are not placed, zero-fills group_list after the non-empty rows and
+// writes err_count; the workgroup owning the last key writes actual_token_num.
+// LDS: the range-order layout (ro_lds_words(kr)), then presence [nb] | first row of each
+// owned key [kr] | session and micro-batch id of each chunk [2][A].
+__global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a, uint32_t nb, uint32_t kr, int nbits,
+                                                                    uint32_t* __restrict__ pos_of,
+                                                                    int64_t* __restrict__ group_list,
+                                                                    int64_t group_rows,
+                                                                    int64_t* __restrict__ actual,
+                                                                    int32_t* __restrict__ err_count) {
+  extern __shared__ uint32_t lds_words[];
+  __shared__ uint32_t wsum[2 * kRoWaves + 2];
+  const uint32_t lo = blockIdx.x * kr;
+  const uint32_t krr = min(kr, nb - lo);
+  uint32_t* cnt = ro_counters(lds_words);
+  uint32_t* pres = cnt + kRoWaves * kr;
+  uint32_t* kfirst = pres + nb;
+  int32_t* ses = reinterpret_cast<int32_t*>(kfirst + kr);
+  const uint32_t nchunks = static_cast<uint32_t>(a.Y / a.chunk);
+  int32_t* mbs = ses + nchunks;
+  const bool g0 = blockIdx.x == 0;
+  const uint32_t plim = g0 ? nb : lo;  // presence is tracked for keys < plim
+  for (int i = threadIdx.x; i < kRoWaves * static_cast<int>(krr); i += kRoThreads) cnt[i] = 0u;
+  for (uint32_t i = threadIdx.x; i < plim; i += kRoThreads) pres[i] = 0u;
+  for (uint32_t c = threadIdx.x; c < nchunks; c += kRoThreads) {
+    ses[c] = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
+    mbs[c] = a.micro_batch_ids ? a.micro_batch_ids[c] : 0;
+  }
+  __syncthreads();
+  const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
+  uint32_t b, e;
+  ro_slice(static_cast<uint32_t>(a.Y), w, b, e);
+  const RoKeysBatching ks{a};
+  const RoWave wv = ro_wave(lds_words, w, krr);
+  uint32_t nerr = 0;
+  uint32_t len;
+  const uint32_t below = ro_count(ks, b, e, lo, krr, wv, len, [&](uint32_t s, uint32_t key, bool v, bool er) {
+    if (v && key < plim) __hip_atomic_store(&pres[key], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (g0) {
+      if (!v) pos_of[s] = kNoRank;
+      nerr += er ? 1u : 0u;
+    }
+  });
+  uint32_t kcount, below_total, end;
+  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, below_total, end);
+  const uint32_t k = threadIdx.x;
+  if (k < krr) kfirst[k] = first;
+  // non-empty keys below lo (workgroup 0: all non-empty keys, lo = 0)
+  uint32_t pcount = 0;
+  for (uint32_t i = k; i < plim; i += kRoThreads) pcount += pres[i];
+  uint32_t ptotal;
+  (void)block_exscan<kRoThreads>(pcount, wsum, ptotal);
+  const uint32_t nz_below = g0 ? 0u : ptotal;
+  const bool nonempty = k < krr && kcount > 0;
+  uint32_t nz_here;
+  const uint32_t row = nz_below + block_exscan<kRoThreads>(nonempty ? 1u : 0u, wsum, nz_here);
+  if (nonempty) {
+    group_list[2 * static_cast<int64_t>(row)] = lo + k;
+    group_list[2 * static_cast<int64_t>(row) + 1] = kcount;
+  }
+  if (g0) {
+    for (int64_t r = static_cast<int64_t>(ptotal) + k; r < group_rows; r += kRoThreads) {
+      group_list[2 * r] = 0;
+      group_list[2 * r + 1] = 0;
+    }
+    uint32_t etot;
+    (void)block_exscan<kRoThreads>(nerr, wsum, etot);
+    if (k == 0 && err_count != nullptr) *err_count = static_cast<int32_t>(etot);
+  }
+  if (k == 0 && lo + krr == nb) *actual = static_cast<int64_t>(end);
+  __syncthreads();  // kfirst
+  const uint32_t chunk = static_cast<uint32_t>(a.chunk);
+  ro_place(ks, b, e, lo, krr, nbits, wv, len, [&](uint32_t s, uint32_t key, uint32_t pos) {
+    const uint32_t c = s / chunk;
+    pos_of[s] = pos;
+    a.token_ids[pos] = static_cast<int32_t>(s);
+    a.offsets[pos] = static_cast<int32_t>(pos - kfirst[key - lo]);
+    a.session_out[pos] = ses[c];
+    a.mb_out[pos] = mbs[c];
+  });
+}
+
+// Row copy after batching_order_kernel: one wavefront per slot; the INT8 scale moves
+// with its row.
+template <int VEC>
+__global__ __launch_bounds__(256) void batching_copy_kernel(BatchArgs a, const uint32_t* __restrict__ pos_of) {
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (s >= a.Y) return;
+  const uint32_t pos = uniform(pos_of[s]);
+  if (pos == kNoRank) return;
+  const uint32_t lane = lane_id();
+  copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+  if (a.dyn_scale != nullptr && lane == 0) a.dyn_scale[pos] = load_scale(a.scale_base + s * a.scale_stride);
 }
 
 // All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
@@ -347,8 +505,15 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
   p->pass = make_pass(Y, nb, bits_for(static_cast<uint64_t>(nb - 1)), 0);
   p->vec = vec_class(reinterpret_cast<uintptr_t>(d->token_data), reinterpret_cast<uintptr_t>(d->y), stride, row, row);
   p->small = (p->pass.nt == 1) && p->pass.R == 4 && nb <= 4096 && Y * row <= (int64_t{1} << 22);
+  // the slot key reads three inputs, so the one-launch order pays off only for moderate
+  // slot counts (measured crossover with the rank / scan / gather path: ~8K slots)
+  p->range_order = !p->small && ro_fits(Y, static_cast<uint64_t>(nb), kBatchingRangeMaxSlots);
   if (p->small) {
     p->ws_bytes = 0;
+  } else if (p->range_order) {
+    Carve c;
+    c.take<uint32_t>(Y);                                              // output row of every slot
+    p->ws_bytes = c.off;
   } else {
     Carve c;
     c.take<uint32_t>(Y);                                              // packed digit / rank
@@ -407,6 +572,22 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
 
   Carve c;
   c.base = static_cast<char*>(ws);
+  if (p.range_order) {
+    uint32_t* pos_of = c.take<uint32_t>(p.Y);
+    const RoPlan rp = ro_plan(static_cast<uint64_t>(nb), kRoGroups);
+    const size_t lds = (ro_lds_words(rp.kr) + nb + rp.kr + 2 * static_cast<size_t>(d->A)) * sizeof(uint32_t);
+    allow_large_lds(reinterpret_cast<const void*>(&batching_order_kernel), lds);
+    hipLaunchKernelGGL(batching_order_kernel, dim3(rp.grid), dim3(kRoThreads), lds, s, a, static_cast<uint32_t>(nb),
+                       rp.kr, rp.nbits, pos_of, d->group_list, d->expert_num, d->actual_token_num, d->err_count);
+    if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
+    const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+    err = launch_vec(p.vec, [&](auto v) {
+      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of);
+    });
+    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+  }
   uint32_t* packed = c.take<uint32_t>(p.Y);
   uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(nb) * p.pass.nt);
   uint32_t* kstart = c.take<uint32_t>(static_cast<size_t>(nb) + 1);
@@ -431,11 +612,11 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
                      static_cast<uint32_t*>(nullptr), tail);
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
+  const Placement pl{packed, hist, kstart, nb, p.pass.tile_shift};
   if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
   const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
   err = launch_vec(p.vec, [&](auto v) {
-    hipLaunchKernelGGL(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, packed, hist,
-                       kstart, nb, p.pass.tile_shift);
+    hipLaunchKernelGGL(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pl);
   });
   if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
   return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;

@@ -65,6 +65,7 @@ struct BatchingPlan {
   const uint8_t* scale_base = nullptr;
   int64_t scale_stride = 0;
   bool small = false;  // single fused workgroup
+  bool range_order = false;  // slot order in one range-partitioned launch, then a row copy
   SortPass pass;
   int vec = 16;        // row copy width class: 16, 4 or 1
   size_t ws_bytes = 0;
@@ -80,6 +81,8 @@ struct UnpermutePlan {
   int elt = 0, pelt = 0;
   bool need_aux = false;     // out_index / permute_token_id requested (non-padded)
   int64_t mask_tiles = 0;    // non-padded probs compaction: token tiles
+  bool mask_fused = false;   // probs compaction in two launches (tile histogram fits LDS)
+  bool range_order = false;  // padded inversion in one range-partitioned launch
   SortPlan sort;             // padded inversion, or non-padded auxiliary order
   size_t ws_bytes = 0;
 };

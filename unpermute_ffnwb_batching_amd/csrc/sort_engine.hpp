@@ -344,26 +344,32 @@ __host__ __device__ inline size_t scan_lds_bytes(int nb) {
   return (static_cast<size_t>(nb) + kScanThreads) * sizeof(uint32_t);
 }
 
-// Output position of element j after a ranking pass and the scan (false if not placed).
-__device__ __forceinline__ bool placed_position(const uint32_t* __restrict__ packed, const uint32_t* __restrict__ off,
-                                                const uint32_t* __restrict__ start, int nb, int tile_shift,
-                                                int64_t j, uint32_t& pos, uint32_t& digit) {
-  const uint32_t p = packed[j];
-  if (p == kNoRank) return false;
-  digit = p >> 16;
-  pos = start[digit] + off[(j >> tile_shift) * nb + digit] + (p & 0xffffu);
-  return true;
-}
+// Output bases of a scanned ranking pass (see scan_hist_kernel).
+struct Placement {
+  const uint32_t* packed;  // per element: digit << 16 | rank in tile, or kNoRank
+  const uint32_t* off;     // [nt * nb] per-digit prefixes over tiles
+  const uint32_t* start;   // [nb + 1] digit starts
+  int nb;
+  int tile_shift;          // tile of element j = j >> tile_shift
+
+  // first position of `digit` in `tile`, minus start[digit]
+  __device__ __forceinline__ uint32_t tile_base(int64_t tile, uint32_t digit) const { return off[tile * nb + digit]; }
+  // output position of element j (false if not placed)
+  __device__ __forceinline__ bool position(int64_t j, uint32_t& pos, uint32_t& digit) const {
+    const uint32_t p = packed[j];
+    if (p == kNoRank) return false;
+    digit = p >> 16;
+    pos = start[digit] + tile_base(j >> tile_shift, digit) + (p & 0xffffu);
+    return true;
+  }
+};
 
 // ------------------------------------------------------------------ LSD scatter passes
 // FINAL = 0: intermediate pass -> keys_out / vals_out.
 // FINAL = 1: last pass of the non-padded auxiliary order -> out_index = val, token = val / K.
 // FINAL = 2: last pass of the padded inversion -> out_index = val, token = sI[val], keys_out.
 template <class KS, bool FIRST, int FINAL>
-__global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t* __restrict__ vals_in,
-                                                          const uint32_t* __restrict__ packed,
-                                                          const uint32_t* __restrict__ off,
-                                                          const uint32_t* __restrict__ start, int nb, int tile_shift,
+__global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t* __restrict__ vals_in, Placement pl,
                                                           int64_t n, uint32_t* __restrict__ keys_out,
                                                           uint32_t* __restrict__ vals_out,
                                                           int32_t* __restrict__ out_index,
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t*
   const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j >= n) return;
   uint32_t pos, digit;
-  if (!placed_position(packed, off, start, nb, tile_shift, j, pos, digit)) return;
+  if (!pl.position(j, pos, digit)) return;
   bool v, e;
   const uint32_t key = ks.key(j, v, e);
   const uint32_t val = FIRST ? static_cast<uint32_t>(j) : vals_in[j];

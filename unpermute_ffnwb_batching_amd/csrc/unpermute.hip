@@ -20,149 +20,11 @@
 #include <type_traits>
 
 #include "internal.hpp"
+#include "range_order.hpp"
+#include "reduce_kernels.hpp"
 #include "sort_engine.hpp"
 
 namespace ffnwb {
-
-enum ReduceMode { kNonPad = 0, kNonPadW2 = 1, kNonPadW1 = 2, kPad = 3, kPadW = 4 };
-
-struct ReduceArgs {
-  const uint8_t* x;
-  int64_t rows, H, T;
-  const int32_t* sI;     // non-padded: slot -> permuted row
-  int32_t K;
-  const uint32_t* seg;   // padded: token segments of the sorted order
-  const int32_t* order;  // padded: sorted position -> permuted row (out_index)
-  const void* w;         // permute_probs (weights), probs element type
-  uint8_t* out;
-};
-
-// One workgroup per token; each thread owns CPT 16-byte chunks of the hidden dimension
-// (or single elements when rows are not 16-byte multiples).  Every wave fetches the
-// token's entry list itself, one entry per lane with a single coalesced load, and marks
-// the valid ones with a ballot; it then walks the valid entries in ascending order, 8 at
-// a time, broadcasting each row index with readlane so that the 8 x CPT row loads of a
-// batch are all in flight before the first one is used.  The weight of each entry is
-// gathered per lane before the row loads and read back with readlane after them.
-template <class TT, class TW, int MODE, int CPT>
-__global__ __launch_bounds__(1024) void unpermute_reduce_kernel(ReduceArgs a) {
-  constexpr bool kPadded = MODE >= kPad;
-  constexpr bool kHasW = (MODE == kNonPadW2) || (MODE == kNonPadW1) || (MODE == kPadW);
-  constexpr int VE = Chunk<TT>::kElems;
-  constexpr int B = 8;
-  const int64_t t = blockIdx.x;
-  const uint32_t lane = lane_id();
-  int64_t ebase, nent;
-  if (kPadded) {
-    ebase = uniform64(static_cast<int64_t>(a.seg[t]));
-    nent = uniform64(static_cast<int64_t>(a.seg[t + 1])) - ebase;
-  } else {
-    ebase = t * a.K;
-    nent = a.K;
-  }
-  const int64_t chunks = a.H * TT::kBytes / 16;
-  const u32x4* __restrict__ x4 = reinterpret_cast<const u32x4*>(a.x);
-  u32x4* __restrict__ o4 = reinterpret_cast<u32x4*>(a.out);
-  for (int64_t c0 = 0; c0 < chunks; c0 += static_cast<int64_t>(CPT) * blockDim.x) {
-    int64_t cidx[CPT];
-    bool cok[CPT];
-    float acc[CPT][VE];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      cidx[i] = c0 + threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
-      cok[i] = cidx[i] < chunks;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[i][e] = 0.0f;
-    }
-    for (int64_t g = 0; g < nent; g += kWave) {
-      const int64_t k = g + lane;
-      int32_t r = 0;
-      bool ok = false;
-      if (k < nent) {
-        const int32_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
-        ok = kPadded || (idx >= 0 && idx < a.rows);
-        r = idx;
-      }
-      float wl = 1.0f;
-      if (kHasW && ok) wl = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : static_cast<int64_t>(r));
-      uint64_t vm = wave_ballot(ok);
-      while (vm != 0) {
-        int32_t rr[B];
-        int lsel[B];
-        int nb = 0;
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          rr[u] = 0;
-          lsel[u] = 0;
-          if (vm != 0) {
-            const int l = static_cast<int>(__builtin_ctzll(vm));
-            vm &= vm - 1;
-            lsel[u] = l;
-            rr[u] = __builtin_amdgcn_readlane(r, l);
-            nb = u + 1;
-          }
-        }
-        u32x4 xv[B][CPT];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          if (u < nb) {
-#pragma unroll
-            for (int i = 0; i < CPT; ++i)
-              if (cok[i]) xv[u][i] = __builtin_nontemporal_load(x4 + static_cast<int64_t>(rr[u]) * chunks + cidx[i]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          if (u < nb) {
-            const float w = kHasW ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), lsel[u])) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-              if (!cok[i]) continue;
-              float f[VE];
-              Chunk<TT>::widen(xv[u][i], f);
-#pragma unroll
-              for (int e = 0; e < VE; ++e) acc[i][e] = kHasW ? acc[i][e] + f[e] * w : acc[i][e] + f[e];
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (cok[i]) o4[t * chunks + cidx[i]] = Chunk<TT>::narrow(acc[i]);
-  }
-}
-
-// Element-wise variant for rows that are not a multiple of 16 bytes (or misaligned).
-template <class TT, class TW, int MODE>
-__global__ __launch_bounds__(1024) void unpermute_reduce_elem_kernel(ReduceArgs a) {
-  constexpr bool kPadded = MODE >= kPad;
-  constexpr bool kHasW = (MODE == kNonPadW2) || (MODE == kNonPadW1) || (MODE == kPadW);
-  const int64_t t = blockIdx.x;
-  int64_t ebase, nent;
-  if (kPadded) {
-    ebase = uniform64(static_cast<int64_t>(a.seg[t]));
-    nent = uniform64(static_cast<int64_t>(a.seg[t + 1])) - ebase;
-  } else {
-    ebase = t * a.K;
-    nent = a.K;
-  }
-  for (int64_t h = threadIdx.x; h < a.H; h += blockDim.x) {
-    float acc = 0.0f;
-    for (int64_t k = 0; k < nent; ++k) {
-      const int64_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
-      if (!kPadded && !(idx >= 0 && idx < a.rows)) continue;
-      const float f = load_elem<TT>(a.x, idx * a.H + h);
-      if (kHasW) {
-        const float w = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : idx);
-        acc = acc + f * w;
-      } else {
-        acc = acc + f;
-      }
-    }
-    store_elem<TT>(a.out, t * a.H + h, acc);
-  }
-}
 
 // Probs compaction (non-padded with probs): permute_probs lists probs[t, e] for the
 // non-zero routing-map entries in expert-major order, i.e. a stable counting sort of
@@ -186,18 +48,16 @@ __global__ __launch_bounds__(256) void mask_count_kernel(const uint8_t* __restri
   }
 }
 
-// permute_probs[start[e] + off[tile*E + e] + running count] = probs[t, e]; entries at
-// positions >= N are dropped; positions from start[E] (the number of non-zero entries)
-// up to N get 0.
+// permute_probs[start[e] + (tile's base for e) + running count] = probs[t, e]; entries
+// at positions >= N are dropped; positions from start[E] (the number of non-zero
+// entries) up to N get 0.  `pl` is the scanned histogram (its packed field is unused).
 template <typename P>
 __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __restrict__ map,
                                                            const P* __restrict__ probs, int64_t T, int32_t E,
-                                                           const uint32_t* __restrict__ off,
-                                                           const uint32_t* __restrict__ start,
-                                                           P* __restrict__ pp, int64_t N) {
+                                                           Placement pl, P* __restrict__ pp, int64_t N) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    uint32_t pos = start[e] + off[static_cast<int64_t>(blockIdx.x) * E + e];
+    uint32_t pos = pl.start[e] + pl.tile_base(blockIdx.x, static_cast<uint32_t>(e));
     // map bytes and probs of the whole tile column are loaded first (clamped rows, no
     // branch), so the loads are in flight together; probs reads are coalesced across e
     uint8_t m[kMaskTile];
@@ -216,20 +76,240 @@ __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __rest
       }
     }
   }
-  const uint32_t filled = start[E];
+  const uint32_t filled = pl.start[E];
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < N;
        g += static_cast<int64_t>(gridDim.x) * blockDim.x)
     if (g >= filled) pp[g] = P(0);
+}
+
+// Probs compaction in two launches, for maps whose tile histogram fits LDS.  Tiles of
+// kMaskRows token rows; a work item is kMaskGroupRows consecutive rows x W consecutive
+// columns (W = 4 when the columns come in aligned groups of 4, else 1), read as one
+// W-byte map load and one W-element probs load per row.
+//   mask_tile_count_kernel   hist[tile*E + e] = non-zero entries of column e in the tile;
+//   mask_compact_kernel      each tile's workgroup copies the whole histogram to LDS,
+//                            derives the column totals, the column starts (one scan over
+//                            the columns) and its own tile prefix, then the start of each
+//                            of its row groups, and places its entries in row order.
+// No scan launch: the histogram is small enough for every workgroup to read it.
+constexpr int kMaskRows = 256;
+constexpr int kMaskGroupRows = 16;
+constexpr int kMaskGroups = kMaskRows / kMaskGroupRows;
+constexpr int kMaskLdsHist = 16384;    // histogram words a compaction workgroup holds
+constexpr int kMaskFusedMaxExperts = 1024;
+
+template <int W>
+__device__ __forceinline__ uint32_t load_map_unit(const uint8_t* p) {
+  if (W == 4) return *reinterpret_cast<const uint32_t*>(p);
+  return *p;
+}
+
+template <int W, typename P>
+struct ProbUnit {
+  P v[W];
+  __device__ __forceinline__ void load(const P* p) {
+    if (W == 4 && sizeof(P) == 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(p);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else if (W == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      v[0] = static_cast<P>(q.x & 0xffffu); v[1] = static_cast<P>(q.x >> 16);
+      v[2] = static_cast<P>(q.y & 0xffffu); v[3] = static_cast<P>(q.y >> 16);
+    } else {
+#pragma unroll
+      for (int w = 0; w < W; ++w) v[w] = p[w];
+    }
+  }
+};
+
+// Loads the map units of one work item (rows clamped to the map) and counts its
+// non-zero entries per column.
+template <int W>
+__device__ __forceinline__ void mask_item_counts(const uint8_t* __restrict__ map, int64_t T, int32_t E, int64_t r0,
+                                                 int c, uint32_t (&x)[kMaskGroupRows], uint32_t (&cnt)[W]) {
+#pragma unroll
+  for (int r = 0; r < kMaskGroupRows; ++r) x[r] = load_map_unit<W>(map + min(r0 + r, T - 1) * E + c * W);
+#pragma unroll
+  for (int w = 0; w < W; ++w) cnt[w] = 0u;
+#pragma unroll
+  for (int r = 0; r < kMaskGroupRows; ++r) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) cnt[w] += (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
+  }
+}
+
+template <int W>
+__global__ __launch_bounds__(256) void mask_tile_count_kernel(const uint8_t* __restrict__ map, int64_t T, int32_t E,
+                                                              uint32_t* __restrict__ hist) {
+  extern __shared__ uint32_t colc[];  // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) colc[e] = 0u;
+  __syncthreads();
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskRows;
+  const int cu = E / W;
+  for (int it = threadIdx.x; it < kMaskGroups * cu; it += blockDim.x) {
+    const int g = it / cu;
+    const int c = it - g * cu;
+    uint32_t x[kMaskGroupRows], cnt[W];
+    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      if (cnt[w] != 0) atomicAdd(&colc[c * W + w], cnt[w]);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = colc[e];
+}
+
+// LDS words of mask_compact_kernel.
+inline size_t mask_compact_lds_words(int ntiles, int E) {
+  return static_cast<size_t>(ntiles) * E + static_cast<size_t>(kMaskGroups) * E + 2 * static_cast<size_t>(E);
+}
+
+constexpr int kMaskCompactThreads = 512;
+
+// One work item's map units and probs, loaded before they are needed.
+template <int W, typename P>
+struct MaskItem {
+  uint32_t x[kMaskGroupRows];
+  ProbUnit<W, P> pv[kMaskGroupRows];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ map, const P* __restrict__ probs, int64_t T,
+                                       int32_t E, int64_t r0, int c) {
+#pragma unroll
+    for (int r = 0; r < kMaskGroupRows; ++r) {
+      const int64_t row = min(r0 + r, T - 1);  // clamped: unconditional loads
+      x[r] = load_map_unit<W>(map + row * E + c * W);
+      pv[r].load(probs + row * E + c * W);
+    }
+  }
+  __device__ __forceinline__ void count(int64_t T, int64_t r0, uint32_t (&cnt)[W]) const {
+#pragma unroll
+    for (int w = 0; w < W; ++w) cnt[w] = 0u;
+#pragma unroll
+    for (int r = 0; r < kMaskGroupRows; ++r) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) cnt[w] += (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
+    }
+  }
+  // writes the item's non-zero entries from positions pos[w] on, rows in order
+  __device__ __forceinline__ void place(int64_t T, int64_t r0, uint32_t (&pos)[W], P* __restrict__ pp,
+                                        int64_t N) const {
+#pragma unroll
+    for (int r = 0; r < kMaskGroupRows; ++r) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) {
+          if (pos[w] < N) pp[pos[w]] = pv[r].v[w];
+          ++pos[w];
+        }
+      }
+    }
+  }
+};
+
+template <int W, typename P>
+__global__ __launch_bounds__(kMaskCompactThreads) void mask_compact_kernel(const uint8_t* __restrict__ map,
+                                                                           const P* __restrict__ probs, int64_t T,
+                                                                           int32_t E, int ntiles,
+                                                                           const uint32_t* __restrict__ hist,
+                                                                           P* __restrict__ pp, int64_t N) {
+  constexpr int NT = kMaskCompactThreads;
+  extern __shared__ uint32_t lds[];
+  uint32_t* h = lds;                     // [ntiles][E] tile histogram
+  uint32_t* gc = h + ntiles * E;         // [kMaskGroups][E] group counts -> group starts
+  uint32_t* tot = gc + kMaskGroups * E;  // [E] column totals
+  uint32_t* tpre = tot + E;              // [E] this tile's prefix per column
+  __shared__ uint32_t wsum[NT / kWave + 1];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t t0 = static_cast<int64_t>(tile) * kMaskRows;
+  const int cu = E / W;
+  const int items = kMaskGroups * cu;
+  const int hw = ntiles * E;
+  // 1. every global load of the first round at once: the first histogram batch and this
+  //    thread's first item (map units and probs)
+  MaskItem<W, P> first;
+  const bool has_first = tid < items;
+  const int g0 = has_first ? tid / cu : 0;
+  const int c0 = has_first ? tid - g0 * cu : 0;
+  first.load(map, probs, T, E, t0 + g0 * kMaskGroupRows, c0);
+  for (int i0 = 0; i0 < hw; i0 += NT * 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = hist[min(i0 + u * NT + tid, hw - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + u * NT + tid < hw) h[i0 + u * NT + tid] = v[u];
+  }
+  if (has_first) {
+    uint32_t cnt[W];
+    first.count(T, t0 + g0 * kMaskGroupRows, cnt);
+#pragma unroll
+    for (int w = 0; w < W; ++w) gc[g0 * E + c0 * W + w] = cnt[w];
+  }
+  for (int it = tid + NT; it < items; it += NT) {  // wide maps: further items one by one
+    const int g = it / cu;
+    const int c = it - g * cu;
+    uint32_t x[kMaskGroupRows], cnt[W];
+    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
+#pragma unroll
+    for (int w = 0; w < W; ++w) gc[g * E + c * W + w] = cnt[w];
+  }
+  __syncthreads();
+  // 2. column totals and tile prefixes; thread i owns the columns [i*per, (i+1)*per)
+  const int per = (E + NT - 1) / NT;
+  const int lo = min(E, tid * per);
+  const int hi = min(E, lo + per);
+  uint32_t mine = 0;
+  for (int e = lo; e < hi; ++e) {
+    uint32_t t_all = 0, t_pre = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const uint32_t v = h[t * E + e];
+      t_pre += (t < tile) ? v : 0u;
+      t_all += v;
+    }
+    tot[e] = t_all;
+    tpre[e] = t_pre;
+    mine += t_all;
+  }
+  uint32_t filled;
+  uint32_t start = block_exscan<NT>(mine, wsum, filled);  // first position of column lo
+  // 3. start of each row group of this tile, per column
+  for (int e = lo; e < hi; ++e) {
+    uint32_t run = start + tpre[e];
+    for (int g = 0; g < kMaskGroups; ++g) {
+      const uint32_t c = gc[g * E + e];
+      gc[g * E + e] = run;
+      run += c;
+    }
+    start += tot[e];
+  }
+  __syncthreads();
+  // 4. place the tile's entries, rows in order within each item
+  if (has_first) {
+    uint32_t pos[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) pos[w] = gc[g0 * E + c0 * W + w];
+    first.place(T, t0 + g0 * kMaskGroupRows, pos, pp, N);
+  }
+  for (int it = tid + NT; it < items; it += NT) {
+    const int g = it / cu;
+    const int c = it - g * cu;
+    MaskItem<W, P> item;
+    item.load(map, probs, T, E, t0 + g * kMaskGroupRows, c);
+    uint32_t pos[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) pos[w] = gc[g * E + c * W + w];
+    item.place(T, t0 + g * kMaskGroupRows, pos, pp, N);
+  }
+  // 5. positions from the number of non-zero entries up to N get 0
+  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * NT + tid; gi < N; gi += static_cast<int64_t>(gridDim.x) * NT)
+    if (gi >= filled) pp[gi] = P(0);
 }
 
 // Padded inversion, single pass: out_index / permute_token_id at the sorted position, and
 // the capacity entry's prob permute_probs[j] = probs[sI[j], j / C] (0 for invalid tokens).
 template <typename P>
 __global__ __launch_bounds__(256) void padded_scatter_kernel(const int32_t* __restrict__ sI, int32_t T,
-                                                             const uint32_t* __restrict__ packed,
-                                                             const uint32_t* __restrict__ off,
-                                                             const uint32_t* __restrict__ start, int nb,
-                                                             int tile_shift, int64_t n,
+                                                             Placement pl, int64_t n,
                                                              int32_t* __restrict__ out_index,
                                                              int32_t* __restrict__ token_out,
                                                              const P* __restrict__ probs, int64_t E, int64_t C,
@@ -238,11 +318,60 @@ __global__ __launch_bounds__(256) void padded_scatter_kernel(const int32_t* __re
   if (j >= n) return;
   const int32_t v = sI[j];
   uint32_t pos, dig;
-  if (placed_position(packed, off, start, nb, tile_shift, j, pos, dig)) {
+  if (pl.position(j, pos, dig)) {
     out_index[pos] = static_cast<int32_t>(j);
     if (token_out != nullptr) token_out[pos] = v;
   }
   if (pp != nullptr) pp[j] = (v >= 0 && v < T) ? probs[static_cast<int64_t>(v) * E + j / C] : P(0);
+}
+
+// Padded inversion in one launch: the range-partitioned order of the capacity entries by
+// token (invalid ids share the last key T).  Workgroup b owns the keys [lo, lo + kr): it
+// writes seg[t], the first sorted position of token t, for its keys, and out_index /
+// permute_token_id at the sorted positions of its entries; the workgroup that owns key T
+// also writes seg[T + 1] = n.  Every workgroup gathers permute_probs for its share of the
+// entries first.
+template <typename P>
+__global__ __launch_bounds__(kRoThreads) void padded_order_kernel(const int32_t* __restrict__ sI, int32_t T,
+                                                                  int64_t n, uint32_t kr, int nbits,
+                                                                  int32_t* __restrict__ order,
+                                                                  int32_t* __restrict__ token_out,
+                                                                  uint32_t* __restrict__ seg,
+                                                                  const P* __restrict__ probs, int64_t E, int64_t C,
+                                                                  P* __restrict__ pp) {
+  extern __shared__ uint32_t lds_words[];  // range-order layout (ro_lds_words)
+  __shared__ uint32_t wsum[2 * kRoWaves + 2];
+  const uint32_t nkeys = static_cast<uint32_t>(T) + 1u;
+  const uint32_t lo = blockIdx.x * kr;
+  const uint32_t krr = min(kr, nkeys - lo);
+  uint32_t* cnt = ro_counters(lds_words);
+  for (int i = threadIdx.x; i < kRoWaves * static_cast<int>(krr); i += kRoThreads) cnt[i] = 0u;
+  if (pp != nullptr) {
+    const int64_t share = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * share;
+    const int64_t j1 = min(n, j0 + share);
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += kRoThreads) {
+      const int32_t v = sI[j];
+      pp[j] = (v >= 0 && v < T) ? probs[static_cast<int64_t>(v) * E + j / C] : P(0);
+    }
+  }
+  __syncthreads();
+  const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
+  uint32_t b, e;
+  ro_slice(static_cast<uint32_t>(n), w, b, e);
+  const RoKeysPadded ks{sI, T, static_cast<uint32_t>(n)};
+  const RoWave wv = ro_wave(lds_words, w, krr);
+  uint32_t len;
+  const uint32_t below = ro_count(ks, b, e, lo, krr, wv, len, [](uint32_t, uint32_t, bool, bool) {});
+  uint32_t kcount, below_total, end;
+  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, below_total, end);
+  if (threadIdx.x < krr) seg[lo + threadIdx.x] = first;
+  if (threadIdx.x == 0 && lo + krr == nkeys) seg[nkeys] = end;
+  ro_place(ks, b, e, lo, krr, nbits, wv, len, [&](uint32_t j, uint32_t key, uint32_t pos) {
+    order[pos] = static_cast<int32_t>(j);
+    // the raw id equals the key except in the invalid bucket: no load on the common path
+    if (token_out != nullptr) token_out[pos] = key < static_cast<uint32_t>(T) ? static_cast<int32_t>(key) : sI[j];
+  });
 }
 
 template <typename P>
@@ -278,11 +407,15 @@ static void launch_rank(const SortPass& p, KS ks, uint32_t* packed, uint32_t* hi
                        p.nbits, p.nb, packed, hist, p.nt, tile_err);
 }
 
-static void launch_scan(const SortPass& p, uint32_t* hist, uint32_t* start, uint32_t* total, hipStream_t s) {
+// Scans a histogram of nb digits x nt tiles and returns where its elements go.
+static Placement launch_scan(int nb, int nt, int tile_shift, const uint32_t* packed, uint32_t* hist, uint32_t* start,
+                             hipStream_t s) {
   ScanTail none{nullptr, 0, nullptr, nullptr, nullptr};
-  const size_t lds = scan_lds_bytes(p.nb);
+  const size_t lds = scan_lds_bytes(nb);
   allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), lds);
-  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), lds, s, hist, p.nb, p.nt, start, total, none);
+  hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), lds, s, hist, nb, nt, start,
+                     static_cast<uint32_t*>(nullptr), none);
+  return Placement{packed, hist, start, nb, tile_shift};
 }
 
 struct SortBufs {
@@ -292,30 +425,42 @@ struct SortBufs {
   uint32_t* kA; uint32_t* vA; uint32_t* kB; uint32_t* vB;
 };
 
+static void carve_sort_bufs(Carve& c, const SortPlan& sp, int64_t n, SortBufs* b) {
+  b->packed = c.take<uint32_t>(n);
+  b->hist = c.take<uint32_t>(sp.hist_words);
+  b->start = c.take<uint32_t>(static_cast<size_t>(sp.max_nb) + 1);
+  if (sp.npasses > 1) {
+    b->kA = c.take<uint32_t>(n); b->vA = c.take<uint32_t>(n);
+    b->kB = c.take<uint32_t>(n); b->vB = c.take<uint32_t>(n);
+  }
+}
+
 // Runs every pass but the scatter of the last one; returns the keys/values of the last
-// pass's input (nullptr for a single pass, whose input is the key source itself).
+// pass's input (nullptr for a single pass, whose input is the key source itself) and the
+// last pass's placement.
 template <class KS>
-static void run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const SortBufs& b, const uint32_t** keys_in,
-                                        const uint32_t** vals_in, hipStream_t s) {
+static Placement run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const SortBufs& b, const uint32_t** keys_in,
+                                             const uint32_t** vals_in, hipStream_t s) {
   const uint32_t* kin = nullptr;
   const uint32_t* vin = nullptr;
   uint32_t* kout = b.kA;
   uint32_t* vout = b.vA;
+  Placement pl{};
   for (int i = 0; i < sp.npasses; ++i) {
     const SortPass& p = sp.pass[i];
     if (i == 0) launch_rank(p, ks0, b.packed, b.hist, nullptr, s);
     else launch_rank(p, KeyArray{kin}, b.packed, b.hist, nullptr, s);
-    launch_scan(p, b.hist, b.start, nullptr, s);
+    pl = launch_scan(p.nb, p.nt, p.tile_shift, b.packed, b.hist, b.start, s);
     if (i == sp.npasses - 1) break;
     const unsigned g = grid_for(p.n, 256);
     if (i == 0)
-      hipLaunchKernelGGL((lsd_scatter_kernel<KS, true, 0>), dim3(g), dim3(256), 0, s, ks0, vin, b.packed, b.hist,
-                         b.start, p.nb, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
-                         static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr), 0);
+      hipLaunchKernelGGL((lsd_scatter_kernel<KS, true, 0>), dim3(g), dim3(256), 0, s, ks0, vin, pl, p.n, kout, vout,
+                         static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                         static_cast<const int32_t*>(nullptr), 0);
     else
-      hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 0>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                         b.packed, b.hist, b.start, p.nb, p.tile_shift, p.n, kout, vout, static_cast<int32_t*>(nullptr),
-                         static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr), 0);
+      hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 0>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin, pl,
+                         p.n, kout, vout, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                         static_cast<const int32_t*>(nullptr), 0);
     kin = kout;
     vin = vout;
     kout = (kout == b.kA) ? b.kB : b.kA;
@@ -323,12 +468,16 @@ static void run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const SortBu
   }
   *keys_in = kin;
   *vals_in = vin;
+  return pl;
 }
 
 // A library-owned stream per device on which the non-padded auxiliary sort runs, forked
 // from and joined back to the caller's stream with events, so that it overlaps the probs
 // compaction and the gather-reduce (it depends only on sortedIndices).  Created on first
 // use at the default priority; the mutex keeps each fork's record/wait pair together.
+// Both streams live on one device, so the events skip the system-scope fence (a
+// device-scope release orders the side stream's writes for the caller's stream); with
+// the fence each record left the stream idle for several microseconds.
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr;
@@ -350,9 +499,10 @@ static SideStream* side_stream_for(hipStream_t caller) {
     (void)hipGetDevice(&cur);
     const bool switch_dev = cur != dev;
     if (switch_dev) (void)hipSetDevice(dev);
+    constexpr unsigned kEvFlags = hipEventDisableTiming | hipEventDisableSystemFence;
     if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&ss.fork, kEvFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, kEvFlags) != hipSuccess) {
       ss.failed = true;
       ss.stream = nullptr;
     }
@@ -403,19 +553,19 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
     }
     if (p->K > 512) return FFNWB_ERR_INNER_NULLPTR;
     if (has_probs) {
-      p->mask_tiles = (p->T + kMaskTile - 1) / kMaskTile;
-      c.take<uint32_t>(static_cast<size_t>(p->E) * p->mask_tiles);           // histogram
-      c.take<uint32_t>(static_cast<size_t>(p->E) + 1);                        // column starts
+      const int64_t fused_tiles = (p->T + kMaskRows - 1) / kMaskRows;
+      p->mask_fused = p->E <= kMaskFusedMaxExperts && fused_tiles * p->E <= kMaskLdsHist;
+      p->mask_tiles = p->mask_fused ? fused_tiles : (p->T + kMaskTile - 1) / kMaskTile;
+      const int nt = static_cast<int>(p->mask_tiles);
+      c.take<uint32_t>(static_cast<size_t>(p->E) * nt);                 // histogram
+      c.take<uint32_t>(static_cast<size_t>(p->E) + 1);                  // column starts (three-launch path)
       if (d->permute_probs == nullptr) c.take<uint8_t>(static_cast<size_t>(p->N) * p->pelt);
     }
     p->need_aux = d->out_index != nullptr || d->permute_token_id != nullptr;
     if (p->need_aux && p->N > 0) {
       p->sort = make_sort_plan(p->N, static_cast<uint64_t>(p->rows) + 1);
-      c.take<uint32_t>(p->N);
-      c.take<uint32_t>(p->sort.hist_words);
-      c.take<uint32_t>(static_cast<size_t>(p->sort.max_nb) + 1);
-      if (p->sort.npasses > 1)
-        for (int i = 0; i < 4; ++i) c.take<uint32_t>(p->N);
+      SortBufs b{};
+      carve_sort_bufs(c, p->sort, p->N, &b);
     }
   } else {
     if (has_probs) {
@@ -429,15 +579,16 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
         log_warn("moe_unpermute: padded mode with topK %lld > experts %lld", (long long)(p->N / p->T),
                  (long long)p->E);
     }
-    p->sort = make_sort_plan(p->N, static_cast<uint64_t>(p->T) + 1);
-    c.take<uint32_t>(p->N);                                // packed
-    c.take<uint32_t>(p->sort.hist_words);                  // histogram
-    c.take<uint32_t>(static_cast<size_t>(p->sort.max_nb) + 1);  // digit starts of a pass
+    p->range_order = ro_fits(p->N, static_cast<uint64_t>(p->T) + 1);
+    if (!p->range_order) {
+      p->sort = make_sort_plan(p->N, static_cast<uint64_t>(p->T) + 1);
+      SortBufs b{};
+      carve_sort_bufs(c, p->sort, p->N, &b);               // sort buffers
+    }
     c.take<uint32_t>(static_cast<size_t>(p->T) + 2);       // token segments
     if (d->out_index == nullptr) c.take<int32_t>(p->N);    // sorted order for the reduce
     if (has_probs && d->permute_probs == nullptr) c.take<uint8_t>(static_cast<size_t>(p->N) * p->pelt);
-    if (p->sort.npasses > 1)
-      for (int i = 0; i < 5; ++i) c.take<uint32_t>(p->N);
+    if (p->sort.npasses > 1) c.take<uint32_t>(p->N);       // sorted keys
   }
   p->ws_bytes = c.off;
   return FFNWB_OK;
@@ -528,15 +679,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     }
     SortBufs b{};
     const bool aux = p.need_aux && p.N > 0;
-    if (aux) {
-      b.packed = c.take<uint32_t>(p.N);
-      b.hist = c.take<uint32_t>(p.sort.hist_words);
-      b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
-      if (p.sort.npasses > 1) {
-        b.kA = c.take<uint32_t>(p.N); b.vA = c.take<uint32_t>(p.N);
-        b.kB = c.take<uint32_t>(p.N); b.vB = c.take<uint32_t>(p.N);
-      }
-    }
+    if (aux) carve_sort_bufs(c, p.sort, p.N, &b);
     // auxiliary order (out_index / permute_token_id) on the side stream
     SideStream* side = nullptr;
     if (aux) {
@@ -551,39 +694,54 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
       }
       KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
       const uint32_t *kin, *vin;
-      run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, as);
-      const SortPass& last = p.sort.pass[p.sort.npasses - 1];
+      const Placement pl = run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, as);
       const unsigned g = grid_for(p.N, 256);
       if (p.sort.npasses == 1)
         hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, as, ks,
-                           static_cast<const uint32_t*>(nullptr), b.packed, b.hist, b.start, last.nb,
-                           last.tile_shift, p.N,
-                           static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
-                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
-      else
-        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, as, KeyArray{kin}, vin,
-                           b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N,
-                           static_cast<uint32_t*>(nullptr),
+                           static_cast<const uint32_t*>(nullptr), pl, p.N, static_cast<uint32_t*>(nullptr),
                            static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
                            static_cast<int32_t>(p.K));
+      else
+        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, as, KeyArray{kin}, vin,
+                           pl, p.N, static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
+                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
       if (side != nullptr && hipEventRecord(side->join, side->stream) != hipSuccess) return FFNWB_ERR_RUNTIME;
     }
     // probs compaction, then the gather-reduce, on the caller's stream
-    if (p.has_probs && nt > 0) {
+    if (p.has_probs && nt > 0 && p.mask_fused) {
+      const uint8_t* map = d->routing_map;
+      const uintptr_t pa = reinterpret_cast<uintptr_t>(d->probs);
+      const bool wide = p.E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0 && pa % (4 * p.pelt) == 0;
+      const int32_t E = static_cast<int32_t>(p.E);
+      const size_t count_lds = static_cast<size_t>(p.E) * sizeof(uint32_t);
+      const size_t lds = mask_compact_lds_words(nt, E) * sizeof(uint32_t);
+      auto go = [&](auto wtag, auto ptag) {
+        constexpr int W = decltype(wtag)::value;
+        using P = decltype(ptag);
+        allow_large_lds(reinterpret_cast<const void*>(&mask_compact_kernel<W, P>), lds);
+        hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt), dim3(256), count_lds, s, map, p.T, E, mhist);
+        hipLaunchKernelGGL((mask_compact_kernel<W, P>), dim3(nt), dim3(kMaskCompactThreads), lds, s, map,
+                           static_cast<const P*>(d->probs), p.T, E, nt, mhist, static_cast<P*>(pprobs), p.N);
+      };
+      if (wide) {
+        if (p.pelt == 4) go(std::integral_constant<int, 4>(), uint32_t());
+        else go(std::integral_constant<int, 4>(), uint16_t());
+      } else {
+        if (p.pelt == 4) go(std::integral_constant<int, 1>(), uint32_t());
+        else go(std::integral_constant<int, 1>(), uint16_t());
+      }
+    } else if (p.has_probs && nt > 0) {
       const int th = static_cast<int>(p.E >= 256 ? 256 : (p.E + 63) / 64 * 64);
       hipLaunchKernelGGL(mask_count_kernel, dim3(nt), dim3(th), 0, s, d->routing_map, p.T,
                          static_cast<int32_t>(p.E), mhist);
-      SortPass mp;
-      mp.nb = static_cast<int>(p.E);
-      mp.nt = nt;
-      launch_scan(mp, mhist, cstart, nullptr, s);
+      const Placement mpl = launch_scan(static_cast<int>(p.E), nt, 0, nullptr, mhist, cstart, s);
       if (p.pelt == 4)
         hipLaunchKernelGGL(mask_scatter_kernel<uint32_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
-                           static_cast<const uint32_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mhist, cstart,
+                           static_cast<const uint32_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mpl,
                            static_cast<uint32_t*>(pprobs), p.N);
       else
         hipLaunchKernelGGL(mask_scatter_kernel<uint16_t>, dim3(nt), dim3(th), 0, s, d->routing_map,
-                           static_cast<const uint16_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mhist, cstart,
+                           static_cast<const uint16_t*>(d->probs), p.T, static_cast<int32_t>(p.E), mpl,
                            static_cast<uint16_t*>(pprobs), p.N);
     }
     ra.sI = sI;
@@ -596,43 +754,48 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
   } else {
     SortBufs b{};
-    b.packed = c.take<uint32_t>(p.N);
-    b.hist = c.take<uint32_t>(p.sort.hist_words);
-    b.start = c.take<uint32_t>(static_cast<size_t>(p.sort.max_nb) + 1);
+    if (!p.range_order) carve_sort_bufs(c, p.sort, p.N, &b);
     uint32_t* seg = c.take<uint32_t>(static_cast<size_t>(p.T) + 2);
     int32_t* order = d->out_index ? d->out_index : c.take<int32_t>(p.N);
     if (p.has_probs && pprobs == nullptr) pprobs = c.take<uint8_t>(static_cast<size_t>(p.N) * p.pelt);
     if (!p.has_probs) pprobs = nullptr;  // nothing to gather without probs
-    uint32_t* skeys = nullptr;
-    if (p.sort.npasses > 1) {
-      b.kA = c.take<uint32_t>(p.N); b.vA = c.take<uint32_t>(p.N);
-      b.kB = c.take<uint32_t>(p.N); b.vB = c.take<uint32_t>(p.N);
-      skeys = c.take<uint32_t>(p.N);
-    }
+    uint32_t* skeys = (p.sort.npasses > 1) ? c.take<uint32_t>(p.N) : nullptr;
     KeyPadded ks{sI, static_cast<int32_t>(p.T)};
     const unsigned g = grid_for(p.N, 256);
     if (p.N == 0) {
       hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(p.T + 2, 256)), dim3(256), 0, s, seg, p.T + 2, 0u);
+    } else if (p.range_order) {
+      const RoPlan rp = ro_plan(static_cast<uint64_t>(p.T) + 1, kRoGroups);
+      const size_t lds = ro_lds_words(rp.kr) * sizeof(uint32_t);
+      if (p.pelt == 4) {
+        allow_large_lds(reinterpret_cast<const void*>(&padded_order_kernel<uint32_t>), lds);
+        hipLaunchKernelGGL(padded_order_kernel<uint32_t>, dim3(rp.grid), dim3(kRoThreads), lds, s, sI,
+                           static_cast<int32_t>(p.T), p.N, rp.kr, rp.nbits, order, d->permute_token_id, seg,
+                           static_cast<const uint32_t*>(d->probs), p.E, p.C, static_cast<uint32_t*>(pprobs));
+      } else {
+        allow_large_lds(reinterpret_cast<const void*>(&padded_order_kernel<uint16_t>), lds);
+        hipLaunchKernelGGL(padded_order_kernel<uint16_t>, dim3(rp.grid), dim3(kRoThreads), lds, s, sI,
+                           static_cast<int32_t>(p.T), p.N, rp.kr, rp.nbits, order, d->permute_token_id, seg,
+                           static_cast<const uint16_t*>(d->probs), p.E, p.C, static_cast<uint16_t*>(pprobs));
+      }
     } else if (p.sort.npasses == 1) {
       const SortPass& ps = p.sort.pass[0];
       launch_rank(ps, ks, b.packed, b.hist, nullptr, s);
-      launch_scan(ps, b.hist, seg, nullptr, s);  // digit starts = token segments
+      // digit starts = token segments
+      const Placement pl = launch_scan(ps.nb, ps.nt, ps.tile_shift, b.packed, b.hist, seg, s);
       if (p.pelt == 4)
         hipLaunchKernelGGL(padded_scatter_kernel<uint32_t>, dim3(g), dim3(256), 0, s, sI, static_cast<int32_t>(p.T),
-                           b.packed, b.hist, seg, ps.nb, ps.tile_shift, p.N, order, d->permute_token_id,
-                           static_cast<const uint32_t*>(d->probs), p.E, p.C, static_cast<uint32_t*>(pprobs));
+                           pl, p.N, order, d->permute_token_id, static_cast<const uint32_t*>(d->probs), p.E, p.C,
+                           static_cast<uint32_t*>(pprobs));
       else
         hipLaunchKernelGGL(padded_scatter_kernel<uint16_t>, dim3(g), dim3(256), 0, s, sI, static_cast<int32_t>(p.T),
-                           b.packed, b.hist, seg, ps.nb, ps.tile_shift, p.N, order, d->permute_token_id,
-                           static_cast<const uint16_t*>(d->probs), p.E, p.C, static_cast<uint16_t*>(pprobs));
+                           pl, p.N, order, d->permute_token_id, static_cast<const uint16_t*>(d->probs), p.E, p.C,
+                           static_cast<uint16_t*>(pprobs));
     } else {
       const uint32_t *kin, *vin;
-      run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, s);
-      const SortPass& last = p.sort.pass[p.sort.npasses - 1];
-      hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 2>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin,
-                         b.packed, b.hist, b.start, last.nb, last.tile_shift, p.N, skeys,
-                         static_cast<uint32_t*>(nullptr),
-                         order, d->permute_token_id, sI, 0);
+      const Placement pl = run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, s);
+      hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 2>), dim3(g), dim3(256), 0, s, KeyArray{kin}, vin, pl,
+                         p.N, skeys, static_cast<uint32_t*>(nullptr), order, d->permute_token_id, sI, 0);
       hipLaunchKernelGGL(segment_bounds_kernel, dim3(grid_for(p.N + 1, 256)), dim3(256), 0, s, skeys, p.N,
                          static_cast<uint32_t>(p.T) + 1u, seg);
       if (p.has_probs) {
