@@ -218,15 +218,15 @@ struct ScanTail {
 constexpr int kScanMaxBuckets = 20480;  // digit totals in LDS: 80 KiB
 
 // Sums (or, with `write`, overwrites with running prefixes starting at `base`) the cells
-// h[t*nb + k] for t in [t0, t1), 16 loads in flight at a time.
+// h[t*nb + k] for t in [t0, t1), B loads in flight at a time (clamped, no branch).
+template <int B = 16>  // wider batches measured slower: one CU's memory pipeline is the limit
 __device__ __forceinline__ uint32_t walk_column(uint32_t* __restrict__ h, int nb, int k, int t0, int t1,
                                                 bool write, uint32_t base) {
-  constexpr int B = 16;
   uint32_t run = base;
   for (int t = t0; t < t1; t += B) {
     uint32_t c[B];
 #pragma unroll
-    for (int u = 0; u < B; ++u) c[u] = h[static_cast<int64_t>(min(t + u, t1 - 1)) * nb + k];  // clamped
+    for (int u = 0; u < B; ++u) c[u] = h[static_cast<int64_t>(min(t + u, t1 - 1)) * nb + k];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       if (t + u < t1) {
