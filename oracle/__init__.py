@@ -7,7 +7,10 @@ what the two operations compute, written from the method's pages:
   API page, "Function description" steps 2-4 and the calculation formula);
 * ``moe_token_unpermute_with_routing_map`` -- the reverse unpermute with optional
   prob-weighted accumulation (MoeTokenUnpermuteWithRoutingMap article, section
-  "Function description and formulas", branches 1-4).
+  "Function description and formulas", branches 1-4);
+* ``moe_token_permute_with_routing_map`` -- the forward permute the same article
+  names in "Operator positioning", defined as the arrangement the unpermute's
+  formulas invert.
 
 It exists to check the HIP library against.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import it;
@@ -21,6 +24,8 @@ Parity status per function (see each module header for the pins):
   the W1 switch and the non-padded ``out_index``/``permute_token_id`` outputs
   are pinned only by properties (ranges, permutation, stability) --
   "parity unpinned" beyond those.
+* ``permute``   -- pinned (round trips through the unpermute oracle, a torch
+  nonzero / cumsum construction, brute force of the capacity blocks).
 """
 
 from .numerics import (  # noqa: F401
@@ -29,3 +34,4 @@ from .numerics import (  # noqa: F401
 )
 from .batching import ffn_worker_batching  # noqa: F401
 from .unpermute import moe_token_unpermute_with_routing_map  # noqa: F401
+from .permute import moe_token_permute_with_routing_map  # noqa: F401

@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a,
                                                                     int64_t* __restrict__ actual,
                                                                     int32_t* __restrict__ err_count) {
   extern __shared__ uint32_t lds_words[];
-  __shared__ uint32_t wsum[2 * kRoWaves + 2];
+  __shared__ uint32_t wsum[3 * kRoWaves + 4];  // block scans of up to 3 sequences
+  __shared__ uint32_t bcast[2];
   const uint32_t lo = blockIdx.x * kr;
   const uint32_t krr = min(kr, nb - lo);
   uint32_t* cnt = ro_counters(lds_words);
@@ -246,9 +247,12 @@ __global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a,
   const uint32_t plim = g0 ? nb : lo;  // presence is tracked for keys < plim
   for (int i = threadIdx.x; i < kRoWaves * static_cast<int>(krr); i += kRoThreads) cnt[i] = 0u;
   for (uint32_t i = threadIdx.x; i < plim; i += kRoThreads) pres[i] = 0u;
-  for (uint32_t c = threadIdx.x; c < nchunks; c += kRoThreads) {
-    ses[c] = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
-    mbs[c] = a.micro_batch_ids ? a.micro_batch_ids[c] : 0;
+  // per-chunk ids (A <= 1024 chunks: one per thread), loaded now, stored to LDS after pass 1
+  const uint32_t cid = threadIdx.x;
+  int32_t ses_v = static_cast<int32_t>(cid), mbs_v = 0;
+  if (cid < nchunks) {
+    if (a.session_ids != nullptr) ses_v = a.session_ids[cid];
+    if (a.micro_batch_ids != nullptr) mbs_v = a.micro_batch_ids[cid];
   }
   __syncthreads();
   const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
@@ -265,19 +269,29 @@ __global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a,
       nerr += er ? 1u : 0u;
     }
   });
-  uint32_t kcount, below_total, end;
-  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, below_total, end);
+  uint32_t kcount, end;
+  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, end);
   const uint32_t k = threadIdx.x;
   if (k < krr) kfirst[k] = first;
-  // non-empty keys below lo (workgroup 0: all non-empty keys, lo = 0)
+  if (cid < nchunks) {
+    ses[cid] = ses_v;
+    mbs[cid] = mbs_v;
+  }
+  // one scan of three sequences: [non-empty owned keys | present keys below plim | bad ids];
+  // thread 0's results give the first two totals
   uint32_t pcount = 0;
   for (uint32_t i = k; i < plim; i += kRoThreads) pcount += pres[i];
-  uint32_t ptotal;
-  (void)block_exscan<kRoThreads>(pcount, wsum, ptotal);
-  const uint32_t nz_below = g0 ? 0u : ptotal;
   const bool nonempty = k < krr && kcount > 0;
-  uint32_t nz_here;
-  const uint32_t row = nz_below + block_exscan<kRoThreads>(nonempty ? 1u : 0u, wsum, nz_here);
+  uint32_t v[3] = {nonempty ? 1u : 0u, pcount, nerr};
+  uint32_t all;
+  block_exscan_multi<kRoThreads, 3>(v, wsum, all);
+  if (k == 0) {
+    bcast[0] = v[1];  // non-empty owned keys
+    bcast[1] = v[2];  // ... plus present keys below plim
+  }
+  __syncthreads();  // bcast; kfirst and the chunk ids for pass 2
+  const uint32_t ptotal = bcast[1] - bcast[0];  // workgroup 0: all non-empty keys
+  const uint32_t row = (g0 ? 0u : ptotal) + v[0];
   if (nonempty) {
     group_list[2 * static_cast<int64_t>(row)] = lo + k;
     group_list[2 * static_cast<int64_t>(row) + 1] = kcount;
@@ -287,12 +301,9 @@ __global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a,
       group_list[2 * r] = 0;
       group_list[2 * r + 1] = 0;
     }
-    uint32_t etot;
-    (void)block_exscan<kRoThreads>(nerr, wsum, etot);
-    if (k == 0 && err_count != nullptr) *err_count = static_cast<int32_t>(etot);
+    if (k == 0 && err_count != nullptr) *err_count = static_cast<int32_t>(all - bcast[1]);
   }
   if (k == 0 && lo + krr == nb) *actual = static_cast<int64_t>(end);
-  __syncthreads();  // kfirst
   const uint32_t chunk = static_cast<uint32_t>(a.chunk);
   ro_place(ks, b, e, lo, krr, nbits, wv, len, [&](uint32_t s, uint32_t key, uint32_t pos) {
     const uint32_t c = s / chunk;

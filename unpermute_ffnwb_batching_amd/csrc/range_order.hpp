@@ -160,10 +160,11 @@ __device__ __forceinline__ uint32_t ro_count(const KS& ks, uint32_t b, uint32_t 
 // Middle step, called by every thread after pass 1 (`cnt` = the counter region, laid
 // out [wave][kr]).  Turns cnt[w*kr + k] into the running position of key lo+k for wave
 // w and returns, for thread k < kr, the first position of key lo+k; key_count = its
-// element count (thread k), below_total = elements below lo, end = the position after
-// the owned keys.
+// element count (thread k), end = the position after the owned keys.  `wsum` holds
+// 2 * kRoWaves + 1 words; it is free again when this returns (the last barrier of the
+// scan follows every read of it).
 __device__ __forceinline__ uint32_t ro_middle(uint32_t* cnt, uint32_t kr, uint32_t below, uint32_t* wsum,
-                                              uint32_t& key_count, uint32_t& below_total, uint32_t& end) {
+                                              uint32_t& key_count, uint32_t& end) {
   __syncthreads();
   const uint32_t k = threadIdx.x;
   uint32_t tot = 0;
@@ -180,9 +181,7 @@ __device__ __forceinline__ uint32_t ro_middle(uint32_t* cnt, uint32_t kr, uint32
   if (k < kr) {
     for (int w = 0; w < kRoWaves; ++w) cnt[w * kr + k] += v[1];
   }
-  if (k == 0) wsum[2 * kRoWaves + 1] = v[1];  // = below total (key 0's start)
   __syncthreads();
-  below_total = wsum[2 * kRoWaves + 1];
   key_count = tot;
   return v[1];
 }

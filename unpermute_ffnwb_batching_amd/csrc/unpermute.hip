@@ -363,8 +363,8 @@ __global__ __launch_bounds__(kRoThreads) void padded_order_kernel(const int32_t*
   const RoWave wv = ro_wave(lds_words, w, krr);
   uint32_t len;
   const uint32_t below = ro_count(ks, b, e, lo, krr, wv, len, [](uint32_t, uint32_t, bool, bool) {});
-  uint32_t kcount, below_total, end;
-  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, below_total, end);
+  uint32_t kcount, end;
+  const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, end);
   if (threadIdx.x < krr) seg[lo + threadIdx.x] = first;
   if (threadIdx.x == 0 && lo + krr == nkeys) seg[nkeys] = end;
   ro_place(ks, b, e, lo, krr, nbits, wv, len, [&](uint32_t j, uint32_t key, uint32_t pos) {
