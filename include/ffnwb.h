@@ -15,6 +15,9 @@
  *                      branches: padded x has-probs), "Parameters",
  *                      "Supplementary notes", "Constraints", "Return values
  *                      and error codes".
+ *   moe_permute     -- the forward permute the same article names in "Operator
+ *                      positioning"; its outputs are the arrangement the
+ *                      unpermute's formulas invert (see its section below).
  *
  * Conventions shared by every entry point
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FFNWB_ABI_VERSION 1
+#define FFNWB_ABI_VERSION 2
 
 /* Status codes.  The first three take the aclnn values both pages list. */
 #define FFNWB_OK                 0
@@ -57,8 +60,8 @@ extern "C" {
 /* Element types. 0..2 are the batching page's tokenDtype values. */
 #define FFNWB_DT_FP16 0
 #define FFNWB_DT_BF16 1
-#define FFNWB_DT_INT8 2 /* batching only: INT8 data with an FP32 dynamic scale per row */
-#define FFNWB_DT_FP32 3 /* unpermute only */
+#define FFNWB_DT_INT8 2 /* batching: INT8 data with an FP32 dynamic scale per row; permute: 1-byte elements */
+#define FFNWB_DT_FP32 3 /* unpermute and permute */
 
 /* ------------------------------------------------------------------------------------------
  * FFN-worker batching (aclnnFfnWorkerBatching API page).
@@ -188,15 +191,70 @@ int moe_unpermute_workspace_size(const moe_unpermute_desc* d, size_t* ws_bytes);
 /* Validates again, then enqueues the unpermute on `stream`. */
 int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * MoE token permute with routing map: the step before the experts that the
+ * MoeTokenUnpermuteWithRoutingMap article names in "Operator positioning" -- tokens
+ * regrouped by expert, so that every expert reads its tokens contiguously, plus the
+ * sorted_indices moe_unpermute takes back.  The page does not specify it further; the
+ * outputs are the arrangement moe_unpermute's formulas invert.
+ *
+ * T = num_tokens, H = hidden, E = num_experts, N = num_out_rows.
+ * Non-padded (padded_mode = 0): N a multiple of T, topK = N / T.
+ *   Row r of permuted_tokens = the token of the r-th non-zero routing-map entry in
+ *   expert-major order (expert ascending, then token ascending); rows past the number
+ *   of non-zero entries are zero; entries past N are dropped.
+ *   sorted_indices[t*topK + k] = the row of token t's k-th expert (experts ascending)
+ *   for k < topK when that row exists (< N); -1 for every other slot.
+ * Padded (padded_mode = 1): N = E * capacity.
+ *   sorted_indices[e*C + j] = the j-th token (ascending) routed to expert e, for j below
+ *   min(C, the expert's token count); -1 for the rest.  Row i of permuted_tokens = token
+ *   row sorted_indices[i], zero where that is -1.  Tokens past the capacity are dropped.
+ * Rows are moved as bytes.  Supported: E <= 256 and ceil(T / 256) * E <= 16384.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct moe_permute_desc {
+  int32_t dtype;             /* element type of the rows: FFNWB_DT_FP16, _BF16, _FP32, or _INT8
+                                (1-byte elements, no scale) */
+  int32_t padded_mode;       /* 0 = token-slot layout, 1 = expert-capacity layout */
+  int64_t num_tokens;        /* T >= 1 */
+  int64_t hidden;            /* H > 0 elements per row */
+  int64_t num_experts;       /* E in [1, 256] */
+  int64_t num_out_rows;      /* N >= 0 (see above) */
+  int64_t capacity;          /* C >= 0, padded mode only */
+  int64_t token_row_stride;  /* bytes between token rows; 0 = H * element size */
+
+  /* Inputs. */
+  const void* tokens;           /* [T] rows of H elements, token_row_stride apart */
+  const uint8_t* routing_map;   /* [T, E] bytes, non-zero = the token is routed to the expert */
+
+  /* Outputs (both required). */
+  void* permuted_tokens;        /* [N, H] of dtype, dense */
+  int32_t* sorted_indices;      /* [N] */
+
+  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
+     the row-copy kernel.  NULL = not recorded. */
+  void* ev_copy_begin;
+  void* ev_copy_end;
+} moe_permute_desc;
+
+/* Validates *d and returns the workspace size in bytes (host only, no device work).
+   Errors: FFNWB_ERR_PARAM_NULLPTR (a pointer is NULL), FFNWB_ERR_PARAM_INVALID (dtype,
+   padded_mode, sizes out of range or outside the supported set above, N not a multiple
+   of T (non-padded) or not E * capacity (padded), stride below the row size). */
+int moe_permute_workspace_size(const moe_permute_desc* d, size_t* ws_bytes);
+
+/* Validates again, then enqueues the permute on `stream`. */
+int moe_permute(const moe_permute_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* ffnwb_status_string(int status);
 
 /* FFNWB_ABI_VERSION of the built library. */
 int ffnwb_abi_version(void);
 
-/* sizeof the two descriptors as compiled into the library (binding self-check). */
+/* sizeof the descriptors as compiled into the library (binding self-check). */
 size_t ffnwb_batching_desc_size(void);
 size_t moe_unpermute_desc_size(void);
+size_t moe_permute_desc_size(void);
 
 #ifdef __cplusplus
 }

@@ -273,5 +273,37 @@ def unpermute_config(n):
     raise ValueError(n)
 
 
+def permute_case(seed, T, K, E, H, dtype, padded=False, C=None, n_t=None, route="uniform", row_pad=0):
+    """Forward-permute input: tokens [T, H] (optionally inside rows of H + row_pad
+    elements), a routing map [T, E] with n_t[t] distinct experts per token (drawn in
+    [0, K] unless given; route "uniform" picks experts uniformly, "skew" favours
+    low-numbered experts), and the output size N = T*K (non-padded) or E*C (padded)."""
+    rng = np.random.default_rng(seed)
+    x = _normal_elements(rng, (T, H + row_pad), dtype) if dtype != INT8 else \
+        rng.integers(-127, 128, size=(T, H + row_pad)).astype(np.int8)
+    if n_t is None:
+        n_t = rng.integers(0, K + 1, size=T)
+    n_t = np.minimum(np.asarray(n_t), E)
+    rmap = np.zeros((T, E), dtype=np.int8)
+    if route == "skew":
+        w = 1.0 / np.arange(1, E + 1) ** 1.2
+        w /= w.sum()
+    for t in range(T):
+        if n_t[t] == 0:
+            continue
+        if route == "skew":
+            rmap[t, rng.choice(E, size=int(n_t[t]), replace=False, p=w)] = 1
+        else:
+            rmap[t, rng.choice(E, size=int(n_t[t]), replace=False)] = 1
+    N = (E * C if C is not None else 0) if padded else T * K
+    return dict(tokens_full=x, H=H, dtype=dtype, routing_map=rmap, padded=padded, C=C, N=N, T=T, E=E, K=K)
+
+
+def permute_config():
+    """Forward permute at the non-padded unpermute workload's shape (T=16384, topK=8,
+    E=128, H=4096 BF16): every token routed to 8 distinct uniform experts."""
+    return permute_case(6, T=16384, K=8, E=128, H=4096, dtype=BF16, n_t=np.full(16384, 8))
+
+
 def config(n):
     return batching_config(n) if n <= 3 else unpermute_config(n)

@@ -178,3 +178,55 @@ def check_unpermute(case, got, ref=None, weight_index=0, aux=True, bit_exact=Tru
         assert np.array_equal(np.asarray(got["permute_probs"]).view(np.uint8),
                               np.asarray(ref["permute_probs"]).view(np.uint8))
     return ref
+
+
+# ----------------------------------------------------------------------------- permute
+
+_ELEM_TORCH = {synth.FP16: torch.float16, synth.BF16: torch.bfloat16, synth.FP32: torch.float32,
+               synth.INT8: torch.int8}
+
+
+def permute_tokens(case):
+    """The [T, H] token rows of a permute case as stored (a strided view when padded)."""
+    return case["tokens_full"][:, :case["H"]]
+
+
+def oracle_permute(case):
+    from oracle import moe_token_permute_with_routing_map
+    return moe_token_permute_with_routing_map(permute_tokens(case), case["routing_map"], case["N"],
+                                              padded_mode=case["padded"], capacity=case["C"])
+
+
+def prepare_permute(case, ev_copy=None):
+    full = case["tokens_full"]
+    if case["dtype"] == synth.BF16:
+        t = dev(full.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = dev(full)
+    tokens = t[:, :case["H"]]
+    N = case["N"]
+    out = {"permuted_tokens": _canary((N, case["H"]), _ELEM_TORCH[case["dtype"]]),
+           "sorted_indices": _canary((N,), torch.int32)}
+    return F.PermuteCall(tokens, dev(case["routing_map"]), padded_mode=case["padded"], num_out_rows=N,
+                         capacity=case["C"] or 0, out=out, ev_copy=ev_copy)
+
+
+def fetch_permute(call):
+    pt = call.out["permuted_tokens"]
+    return {"permuted_tokens": _bytes(pt).reshape(pt.shape[0], pt.shape[1] * pt.element_size()),
+            "sorted_indices": call.out["sorted_indices"].cpu().numpy()}
+
+
+def run_permute(case):
+    call = prepare_permute(case)
+    call.run()
+    torch.cuda.synchronize()
+    return fetch_permute(call)
+
+
+def check_permute(case, got, ref=None):
+    ref = ref if ref is not None else oracle_permute(case)
+    assert np.array_equal(got["sorted_indices"], ref["sorted_indices"]), "sorted_indices differ"
+    rb = np.ascontiguousarray(ref["permuted_tokens"]).view(np.uint8).reshape(got["permuted_tokens"].shape)
+    assert np.array_equal(got["permuted_tokens"], rb), "permuted rows differ"
+    return ref

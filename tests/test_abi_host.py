@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
     for n in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
-              "moe_unpermute", "ffnwb_status_string", "ffnwb_abi_version"):
+              "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_status_string",
+              "ffnwb_abi_version"):
         assert n in names
 
 
@@ -37,7 +38,8 @@ def test_descriptor_layout_and_version():
     L = F.lib()
     assert L.ffnwb_batching_desc_size() == ctypes.sizeof(F.BatchingDesc)
     assert L.moe_unpermute_desc_size() == ctypes.sizeof(F.UnpermuteDesc)
-    assert F.ffnwb_abi_version() == 1
+    assert L.moe_permute_desc_size() == ctypes.sizeof(F.PermuteDesc)
+    assert F.ffnwb_abi_version() == 2
     for st in (0, 161001, 161002, 561103, 1, 2):
         assert F.ffnwb_status_string(st).startswith("FFNWB_")
 
@@ -191,3 +193,59 @@ def test_unpermute_workspace_skips_aux_sort_when_not_requested():
     lean = _uws(_unpermute_desc(num_tokens=16384, num_rows=131072, num_indices=131072, num_experts=128,
                                 out_index=None, permute_token_id=None))[1]
     assert lean < full
+
+
+# ----------------------------------------------------------------------------- permute
+
+def _permute_desc(**over):
+    d = F.PermuteDesc()
+    vals = dict(dtype=1, padded_mode=0, num_tokens=64, hidden=32, num_experts=8, num_out_rows=128, capacity=0,
+                token_row_stride=0)
+    vals.update({k: v for k, v in over.items() if k in vals})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    for p in ("tokens", "routing_map", "permuted_tokens", "sorted_indices"):
+        setattr(d, p, FAKE)
+    for k, v in over.items():
+        if k not in vals:
+            setattr(d, k, v)
+    return d
+
+
+def _pws(d):
+    n = ctypes.c_size_t(0)
+    st = F.lib().moe_permute_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_permute_valid_cases():
+    assert _pws(_permute_desc())[0] == 0
+    for dt in (0, 1, 2, 3):
+        assert _pws(_permute_desc(dtype=dt))[0] == 0
+    assert _pws(_permute_desc(padded_mode=1, num_out_rows=8 * 20, capacity=20))[0] == 0
+    assert _pws(_permute_desc(num_out_rows=0))[0] == 0                              # topK = 0
+    assert _pws(_permute_desc(num_experts=256, num_tokens=16384, num_out_rows=16384 * 8))[0] == 0
+    assert _pws(_permute_desc(token_row_stride=96))[0] == 0
+
+
+@pytest.mark.parametrize("field", ["tokens", "routing_map", "permuted_tokens", "sorted_indices"])
+def test_permute_required_pointers(field):
+    assert _pws(_permute_desc(**{field: None}))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+
+
+@pytest.mark.parametrize("over", [
+    dict(dtype=9), dict(padded_mode=3), dict(num_tokens=0), dict(hidden=0), dict(num_experts=0),
+    dict(num_experts=257), dict(num_out_rows=100),                    # not a multiple of T
+    dict(padded_mode=1, num_out_rows=100, capacity=20),               # not E * C
+    dict(num_experts=256, num_tokens=16385, num_out_rows=16385),      # histogram beyond LDS
+    dict(token_row_stride=63), dict(capacity=-1),
+])
+def test_permute_invalid_parameters(over):
+    assert _pws(_permute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_permute_workspace():
+    st, n = _pws(_permute_desc(num_tokens=16384, num_experts=128, num_out_rows=16384 * 8))
+    assert st == 0 and n >= 4 * 16384 * 8            # source token of every row
+    st, n = _pws(_permute_desc(padded_mode=1, num_tokens=8192, num_experts=64, num_out_rows=64 * 512, capacity=512))
+    assert st == 0 and n >= 4 * 32 * 64               # tile histogram only

@@ -7,12 +7,13 @@ The names mirror the C ABI:
 
 * ``ffnwb_batching_workspace_size`` / ``ffnwb_batching``
 * ``moe_unpermute_workspace_size`` / ``moe_unpermute``
+* ``moe_permute_workspace_size`` / ``moe_permute``
 * ``ffnwb_status_string``, ``ffnwb_abi_version``
 
-``ffnwb_batching`` and ``moe_unpermute`` take torch tensors, allocate any output or
-workspace the caller did not pass, fill the C descriptor and enqueue the call on the
-current stream.  ``BatchingCall`` / ``UnpermuteCall`` build the descriptor once for
-repeated launches (benchmarks, graph capture).
+``ffnwb_batching``, ``moe_unpermute`` and ``moe_permute`` take torch tensors, allocate any
+output or workspace the caller did not pass, fill the C descriptor and enqueue the call
+on the current stream.  ``BatchingCall`` / ``UnpermuteCall`` / ``PermuteCall`` build the
+descriptor once for repeated launches (benchmarks, graph capture).
 
 The library must be built (``python -m unpermute_ffnwb_batching_amd.build``); importing
 works without it, but every call then raises ``RuntimeError``: there is no fallback.
@@ -27,7 +28,7 @@ from . import _abi
 from ._abi import (FFNWB_OK, FFNWB_ERR_PARAM_NULLPTR, FFNWB_ERR_PARAM_INVALID,  # noqa: F401
                    FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME,
                    FFNWB_DT_FP16, FFNWB_DT_BF16, FFNWB_DT_INT8, FFNWB_DT_FP32,
-                   BatchingDesc, UnpermuteDesc)
+                   BatchingDesc, UnpermuteDesc, PermuteDesc)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libffnwb.so")
 _lib = None
@@ -52,15 +53,19 @@ def lib():
         L.ffnwb_batching.argtypes = [ctypes.POINTER(BatchingDesc), vp, sz, vp]
         L.moe_unpermute_workspace_size.argtypes = [ctypes.POINTER(UnpermuteDesc), ctypes.POINTER(sz)]
         L.moe_unpermute.argtypes = [ctypes.POINTER(UnpermuteDesc), vp, sz, vp]
+        L.moe_permute_workspace_size.argtypes = [ctypes.POINTER(PermuteDesc), ctypes.POINTER(sz)]
+        L.moe_permute.argtypes = [ctypes.POINTER(PermuteDesc), vp, sz, vp]
         for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
-                  "moe_unpermute", "ffnwb_abi_version"):
+                  "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.ffnwb_status_string.argtypes = [ctypes.c_int]
         L.ffnwb_status_string.restype = ctypes.c_char_p
         L.ffnwb_batching_desc_size.restype = sz
         L.moe_unpermute_desc_size.restype = sz
+        L.moe_permute_desc_size.restype = sz
         if L.ffnwb_batching_desc_size() != ctypes.sizeof(BatchingDesc) or \
-                L.moe_unpermute_desc_size() != ctypes.sizeof(UnpermuteDesc):
+                L.moe_unpermute_desc_size() != ctypes.sizeof(UnpermuteDesc) or \
+                L.moe_permute_desc_size() != ctypes.sizeof(PermuteDesc):
             raise RuntimeError("libffnwb descriptor layout does not match the Python binding")
         if L.ffnwb_abi_version() != _abi.FFNWB_ABI_VERSION:
             raise RuntimeError("libffnwb ABI version mismatch")
@@ -296,3 +301,78 @@ class UnpermuteCall:
 def moe_unpermute(permuted_tokens, sorted_indices, routing_map=None, probs=None, *, stream=None, **kw):
     """Run the unpermute once; returns dict(unpermuted, out_index, permute_token_id, permute_probs)."""
     return UnpermuteCall(permuted_tokens, sorted_indices, routing_map, probs, **kw).run(stream)
+
+
+# ----------------------------------------------------------------------------- permute
+
+_ANY_CODE = {torch.float16: FFNWB_DT_FP16, torch.bfloat16: FFNWB_DT_BF16, torch.float32: FFNWB_DT_FP32,
+             torch.int8: FFNWB_DT_INT8, torch.uint8: FFNWB_DT_INT8}
+
+
+def moe_permute_workspace_size(desc):
+    n = ctypes.c_size_t(0)
+    st = lib().moe_permute_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != FFNWB_OK:
+        raise FfnwbError(st, "moe_permute_workspace_size")
+    return n.value
+
+
+class PermuteCall:
+    """A prepared moe_permute call.
+
+    ``tokens`` [T, H] (fp16 / bf16 / fp32 / int8 / uint8; rows may be strided),
+    ``routing_map`` int8/uint8/bool [T, E].  Non-padded: ``num_out_rows`` = T * topK;
+    padded: ``capacity`` C gives num_out_rows = E * C.
+    """
+
+    def __init__(self, tokens, routing_map, *, padded_mode=False, num_out_rows=None, capacity=0, out=None,
+                 workspace=None, ev_copy=None):
+        T, H = tokens.shape[0], tokens.shape[1]
+        E = routing_map.shape[1]
+        dev = tokens.device
+        N = int(E * capacity) if padded_mode else int(num_out_rows)
+        out = dict(out or {})
+        if "permuted_tokens" not in out:
+            out["permuted_tokens"] = torch.empty((N, H), dtype=tokens.dtype, device=dev)
+        if "sorted_indices" not in out:
+            out["sorted_indices"] = torch.empty(N, dtype=torch.int32, device=dev)
+        self.out = out
+        rm = routing_map.view(torch.uint8) if routing_map.dtype in (torch.bool, torch.int8) else routing_map
+        self._keep = [tokens, rm]
+        d = PermuteDesc()
+        d.dtype = _ANY_CODE.get(tokens.dtype, -1)
+        d.padded_mode = int(bool(padded_mode))
+        d.num_tokens = T
+        d.hidden = H
+        d.num_experts = E
+        d.num_out_rows = N
+        d.capacity = int(capacity)
+        d.token_row_stride = _row_stride_bytes(tokens)
+        d.tokens = _ptr(tokens)
+        d.routing_map = _ptr(rm)
+        d.permuted_tokens = _ptr(out["permuted_tokens"])
+        d.sorted_indices = _ptr(out["sorted_indices"])
+        if ev_copy is not None:
+            d.ev_copy_begin = _event_handle(ev_copy[0])
+            d.ev_copy_end = _event_handle(ev_copy[1])
+        self.desc = d
+        self.ws_bytes = moe_permute_workspace_size(d)
+        if workspace is None and self.ws_bytes:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+
+    def set_copy_events(self, begin, end):
+        self.desc.ev_copy_begin = _event_handle(begin)
+        self.desc.ev_copy_end = _event_handle(end)
+
+    def run(self, stream=None):
+        st = lib().moe_permute(ctypes.byref(self.desc), _ptr(self.workspace), ctypes.c_size_t(self.ws_bytes),
+                               _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "moe_permute")
+        return self.out
+
+
+def moe_permute(tokens, routing_map, *, stream=None, **kw):
+    """Run the forward permute once; returns dict(permuted_tokens, sorted_indices)."""
+    return PermuteCall(tokens, routing_map, **kw).run(stream)

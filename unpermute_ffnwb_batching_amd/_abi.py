@@ -1,8 +1,8 @@
-"""ctypes mirror of include/ffnwb.h (constants and the two descriptor structs)."""
+"""ctypes mirror of include/ffnwb.h (constants and the descriptor structs)."""
 
 import ctypes
 
-FFNWB_ABI_VERSION = 1
+FFNWB_ABI_VERSION = 2
 
 FFNWB_OK = 0
 FFNWB_ERR_PARAM_NULLPTR = 161001
@@ -44,4 +44,15 @@ class UnpermuteDesc(ctypes.Structure):
         ("unpermuted_tokens", _vp), ("out_index", _vp), ("permute_token_id", _vp),
         ("permute_probs", _vp),
         ("ev_reduce_begin", _vp), ("ev_reduce_end", _vp),
+    ]
+
+
+class PermuteDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", _i32), ("padded_mode", _i32),
+        ("num_tokens", _i64), ("hidden", _i64), ("num_experts", _i64), ("num_out_rows", _i64),
+        ("capacity", _i64), ("token_row_stride", _i64),
+        ("tokens", _vp), ("routing_map", _vp),
+        ("permuted_tokens", _vp), ("sorted_indices", _vp),
+        ("ev_copy_begin", _vp), ("ev_copy_end", _vp),
     ]

@@ -36,6 +36,8 @@ size_t ffnwb_batching_desc_size(void) { return sizeof(ffnwb_batching_desc); }
 
 size_t moe_unpermute_desc_size(void) { return sizeof(moe_unpermute_desc); }
 
+size_t moe_permute_desc_size(void) { return sizeof(moe_permute_desc); }
+
 const char* ffnwb_status_string(int status) {
   switch (status) {
     case FFNWB_OK: return "FFNWB_OK";
@@ -80,6 +82,23 @@ int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes,
   if (st != FFNWB_OK) return st;
   if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
   return launch_unpermute(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute_workspace_size(const moe_permute_desc* d, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  PermutePlan p;
+  const int st = plan_permute(d, &p);
+  if (st != FFNWB_OK) return st;
+  *ws_bytes = p.ws_bytes;
+  return FFNWB_OK;
+}
+
+int moe_permute(const moe_permute_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  PermutePlan p;
+  const int st = plan_permute(d, &p);
+  if (st != FFNWB_OK) return st;
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  return launch_permute(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

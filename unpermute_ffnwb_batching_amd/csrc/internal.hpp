@@ -90,6 +90,26 @@ struct UnpermutePlan {
 int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p);
 int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* ws, hipStream_t s);
 
+struct PermutePlan {
+  int64_t T = 0, E = 0, N = 0, K = 0, ntiles = 0;
+  int64_t row_bytes = 0, stride = 0;
+  bool padded = false;
+  size_t ws_bytes = 0;
+};
+
+int plan_permute(const moe_permute_desc* d, PermutePlan* p);
+int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hipStream_t s);
+
+// Widest row-copy access (16, 4 or 1 bytes) that two base addresses, two strides and the
+// row size all allow.
+inline int vec_class(uintptr_t a, uintptr_t b, int64_t s1, int64_t s2, int64_t bytes) {
+  const uint64_t m = static_cast<uint64_t>(a | b | static_cast<uint64_t>(s1) | static_cast<uint64_t>(s2) |
+                                           static_cast<uint64_t>(bytes));
+  if ((m & 15) == 0) return 16;
+  if ((m & 3) == 0) return 4;
+  return 1;
+}
+
 bool log_enabled();
 
 // Records an optional timing event (a hipEvent_t passed as void*) on stream s.

@@ -1,0 +1,302 @@
+// Forward MoE token permute with routing map on gfx950.  The MoeTokenUnpermuteWithRoutingMap
+// article names this step in "Operator positioning" (tokens regrouped by expert so that each
+// expert reads its tokens contiguously; sortedIndices for the way back); its outputs are the
+// arrangement the unpermute's formulas ("Function description and formulas", branches 1-4)
+// invert.
+//
+// Three launches:
+//   1. mask_tile_count_kernel: per tile of kMaskRows tokens, the non-zero entries of every
+//      expert column (map_tiles.hpp);
+//   2. permute_order_kernel: one workgroup per tile copies the whole tile histogram to LDS,
+//      derives the column totals, the column starts and its own tile prefix, and gives
+//      every non-zero entry (t, e) of its tile a place:
+//        non-padded  row r = start[e] + (entries of column e in earlier tiles) + (entries
+//                    of column e in earlier rows of this tile); source_of[r] = t;
+//        padded      position j of the entry within expert e's capacity block;
+//                    sorted_indices[e*C + j] = t while j < C.
+//      Non-padded, a token's rows rise with its expert (rows are expert-major), so its
+//      slots are its entries in ascending expert order: each row of the tile is walked
+//      once more, and slot k takes the row of the k-th entry, whose offset inside the tile
+//      was kept in LDS (one byte per row and expert);
+//   3. permute_rows_kernel: one wavefront per output row copies its source token row, or
+//      writes zeros.
+#include <stdio.h>
+
+#include "internal.hpp"
+#include "map_tiles.hpp"
+#include "row_copy.hpp"
+#include "sort_engine.hpp"
+
+namespace ffnwb {
+
+constexpr int kPermuteThreads = 512;
+constexpr int kPermuteMaxExperts = 256;
+
+// LDS bytes of permute_order_kernel.
+inline size_t permute_order_lds_bytes(int ntiles, int E, bool padded) {
+  const size_t words = static_cast<size_t>(ntiles) * E + static_cast<size_t>(kMaskGroups) * E + 2 * static_cast<size_t>(E);
+  return words * sizeof(uint32_t) + (padded ? 0 : static_cast<size_t>(kMaskRows) * E);
+}
+
+template <int W, bool PADDED>
+__global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const uint8_t* __restrict__ map, int64_t T,
+                                                                        int32_t E, int ntiles,
+                                                                        const uint32_t* __restrict__ hist,
+                                                                        int64_t N, int32_t K, int64_t C,
+                                                                        int32_t* __restrict__ source_of,
+                                                                        int32_t* __restrict__ sorted_indices) {
+  constexpr int NT = kPermuteThreads;
+  extern __shared__ uint32_t lds[];
+  uint32_t* h = lds;                     // [ntiles][E] tile histogram
+  uint32_t* gc = h + ntiles * E;         // [kMaskGroups][E] group counts -> offsets in the tile
+  uint32_t* tot = gc + kMaskGroups * E;  // [E] column totals
+  uint32_t* base = tot + E;              // [E] first place of column e's entries of this tile
+  uint8_t* inoff = reinterpret_cast<uint8_t*>(base + E);  // [kMaskRows][E] (non-padded)
+  __shared__ uint32_t wsum[NT / kWave + 1];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t t0 = static_cast<int64_t>(tile) * kMaskRows;
+  const int cu = E / W;
+  const int items = kMaskGroups * cu;
+  const int hw = ntiles * E;
+  // 1. the histogram to LDS (16 loads in flight per thread, clamped) and this tile's
+  //    per-group counts
+  for (int i0 = 0; i0 < hw; i0 += NT * 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = hist[min(i0 + u * NT + tid, hw - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + u * NT + tid < hw) h[i0 + u * NT + tid] = v[u];
+  }
+  for (int it = tid; it < items; it += NT) {
+    const int g = it / cu;
+    const int c = it - g * cu;
+    uint32_t x[kMaskGroupRows], cnt[W];
+    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
+#pragma unroll
+    for (int w = 0; w < W; ++w) gc[g * E + c * W + w] = cnt[w];
+  }
+  __syncthreads();
+  // 2. column totals and this tile's prefix; thread i owns the columns [i*per, (i+1)*per)
+  const int per = (E + NT - 1) / NT;
+  const int lo = min(E, tid * per);
+  const int hi = min(E, lo + per);
+  uint32_t mine = 0;
+  for (int e = lo; e < hi; ++e) {
+    uint32_t t_all = 0, t_pre = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const uint32_t v = h[t * E + e];
+      t_pre += (t < tile) ? v : 0u;
+      t_all += v;
+    }
+    tot[e] = t_all;
+    base[e] = t_pre;
+    mine += t_all;
+  }
+  uint32_t filled;
+  uint32_t start = block_exscan<NT>(mine, wsum, filled);  // first row of column lo (non-padded)
+  for (int e = lo; e < hi; ++e) {
+    if (!PADDED) base[e] += start;
+    start += tot[e];
+    uint32_t run = 0;
+    for (int g = 0; g < kMaskGroups; ++g) {
+      const uint32_t c = gc[g * E + e];
+      gc[g * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // 3. a place for every entry of the tile, rows in order within each item
+  for (int it = tid; it < items; it += NT) {
+    const int g = it / cu;
+    const int c = it - g * cu;
+    const int64_t r0 = t0 + g * kMaskGroupRows;
+    uint32_t x[kMaskGroupRows], cnt[W];
+    mask_item_counts<W>(map, T, E, r0, c, x, cnt);
+    uint32_t off[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) off[w] = gc[g * E + c * W + w];
+#pragma unroll
+    for (int r = 0; r < kMaskGroupRows; ++r) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) {
+          const int e = c * W + w;
+          const uint32_t place = base[e] + off[w];
+          if (PADDED) {
+            if (place < static_cast<uint64_t>(C)) sorted_indices[e * C + place] = static_cast<int32_t>(r0 + r);
+          } else {
+            if (place < static_cast<uint64_t>(N)) source_of[place] = static_cast<int32_t>(r0 + r);
+            inoff[(g * kMaskGroupRows + r) * E + e] = static_cast<uint8_t>(off[w]);
+          }
+          ++off[w];
+        }
+      }
+    }
+  }
+  if (PADDED) {
+    // 4. unused capacity: -1 (every workgroup takes a share of the E*C places)
+    const int64_t all = static_cast<int64_t>(E) * C;
+    for (int64_t i = static_cast<int64_t>(tile) * NT + tid; i < all; i += static_cast<int64_t>(gridDim.x) * NT) {
+      const int32_t e = static_cast<int32_t>(i / C);
+      if (i - static_cast<int64_t>(e) * C >= static_cast<int64_t>(tot[e])) sorted_indices[i] = -1;
+    }
+    return;
+  }
+  __syncthreads();
+  // 4. the slots of each token of the tile: its entries in ascending expert order
+  for (int rr = tid; rr < kMaskRows; rr += NT) {
+    const int64_t t = t0 + rr;
+    if (t >= T) break;
+    const uint8_t* row = map + t * E;
+    int32_t k = 0;
+    for (int c0 = 0; c0 < cu; c0 += 16) {
+      uint32_t x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = load_map_unit<W>(row + min(c0 + u, cu - 1) * W);  // clamped
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (c0 + u >= cu) continue;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          if (((x[u] >> (8 * w)) & 0xffu) != 0) {
+            const int e = (c0 + u) * W + w;
+            const uint32_t r = base[e] + inoff[rr * E + e];
+            if (k < K) sorted_indices[t * K + k] = (r < static_cast<uint64_t>(N)) ? static_cast<int32_t>(r) : -1;
+            ++k;
+          }
+        }
+      }
+    }
+    for (; k < K; ++k) sorted_indices[t * K + k] = -1;
+  }
+  // 5. rows past the non-zero entries have no source
+  for (int64_t r = static_cast<int64_t>(tile) * NT + tid; r < N; r += static_cast<int64_t>(gridDim.x) * NT)
+    if (r >= filled) source_of[r] = -1;
+}
+
+// One wavefront per output row: the source token's row, or zeros.
+template <int VEC>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
+                                                           int64_t row_bytes, const int32_t* __restrict__ source_of,
+                                                           int64_t N, uint8_t* __restrict__ out) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (r >= N) return;
+  const int32_t src = uniform(source_of[r]);
+  const uint32_t lane = lane_id();
+  uint8_t* dst = out + r * row_bytes;
+  if (src >= 0) {
+    copy_row<VEC>(tokens + static_cast<int64_t>(src) * stride, dst, row_bytes, lane);
+    return;
+  }
+  if (VEC == 1) {
+    for (int64_t i = lane; i < row_bytes; i += kWave) dst[i] = 0;
+    return;
+  }
+  typedef typename RowVec<VEC>::type V;
+  V* d4 = reinterpret_cast<V*>(dst);
+  const int64_t n16 = row_bytes >> 4;
+  const V z = {0u, 0u, 0u, 0u};
+  for (int64_t i = lane; i < n16; i += kWave) __builtin_nontemporal_store(z, d4 + i);
+  if (VEC == 4) {
+    const int64_t tail = (row_bytes & 15) >> 2;
+    if (lane < tail) reinterpret_cast<uint32_t*>(dst + n16 * 16)[lane] = 0u;
+  }
+}
+
+static int element_bytes(int dtype) {
+  switch (dtype) {
+    case FFNWB_DT_FP16: case FFNWB_DT_BF16: return 2;
+    case FFNWB_DT_INT8: return 1;
+    case FFNWB_DT_FP32: return 4;
+    default: return 0;
+  }
+}
+
+int plan_permute(const moe_permute_desc* d, PermutePlan* p) {
+  if (d == nullptr || p == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  if (d->tokens == nullptr || d->routing_map == nullptr || d->permuted_tokens == nullptr ||
+      d->sorted_indices == nullptr)
+    return FFNWB_ERR_PARAM_NULLPTR;
+  const int elt = element_bytes(d->dtype);
+  if (elt == 0) return FFNWB_ERR_PARAM_INVALID;
+  if (d->padded_mode != 0 && d->padded_mode != 1) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t T = d->num_tokens, H = d->hidden, E = d->num_experts, N = d->num_out_rows;
+  if (T < 1 || H < 1 || E < 1 || E > kPermuteMaxExperts || N < 0 || d->capacity < 0) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  if (T > lim / E || N > lim || H > (int64_t{1} << 30)) return FFNWB_ERR_PARAM_INVALID;
+  const int64_t ntiles = (T + kMaskRows - 1) / kMaskRows;
+  if (ntiles * E > kMaskLdsHist) return FFNWB_ERR_PARAM_INVALID;
+  p->padded = d->padded_mode == 1;
+  if (p->padded) {
+    if (N != E * d->capacity) return FFNWB_ERR_PARAM_INVALID;
+    p->K = 0;
+  } else {
+    if (N % T != 0) return FFNWB_ERR_PARAM_INVALID;
+    p->K = N / T;
+  }
+  p->row_bytes = H * elt;
+  p->stride = d->token_row_stride ? d->token_row_stride : p->row_bytes;
+  if (p->stride < p->row_bytes) return FFNWB_ERR_PARAM_INVALID;
+  if (static_cast<double>(T) * p->stride > 9.0e18 || static_cast<double>(N) * p->row_bytes > 9.0e18)
+    return FFNWB_ERR_PARAM_INVALID;
+  p->T = T;
+  p->E = E;
+  p->N = N;
+  p->ntiles = ntiles;
+  Carve c;
+  c.take<uint32_t>(static_cast<size_t>(ntiles * E));       // tile histogram
+  if (!p->padded) c.take<int32_t>(static_cast<size_t>(N));  // source token of every row
+  p->ws_bytes = c.off;
+  return FFNWB_OK;
+}
+
+int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hipStream_t s) {
+  if (p.N == 0) return FFNWB_OK;
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.ntiles * p.E));
+  int32_t* source_of = p.padded ? d->sorted_indices : c.take<int32_t>(static_cast<size_t>(p.N));
+  const uint8_t* map = d->routing_map;
+  const int32_t E = static_cast<int32_t>(p.E);
+  const int nt = static_cast<int>(p.ntiles);
+  const bool wide = E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0;
+  const size_t count_lds = static_cast<size_t>(E) * sizeof(uint32_t);
+  const size_t lds = permute_order_lds_bytes(nt, E, p.padded);
+  auto go = [&](auto wtag, auto ptag) {
+    constexpr int W = decltype(wtag)::value;
+    constexpr bool PADDED = decltype(ptag)::value;
+    allow_large_lds(reinterpret_cast<const void*>(&permute_order_kernel<W, PADDED>), lds);
+    hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt), dim3(256), count_lds, s, map, p.T, E, hist);
+    hipLaunchKernelGGL((permute_order_kernel<W, PADDED>), dim3(nt), dim3(kPermuteThreads), lds, s, map, p.T, E, nt,
+                       hist, p.N, static_cast<int32_t>(p.K), d->capacity, source_of, d->sorted_indices);
+  };
+  if (wide) {
+    if (p.padded) go(std::integral_constant<int, 4>(), std::true_type());
+    else go(std::integral_constant<int, 4>(), std::false_type());
+  } else {
+    if (p.padded) go(std::integral_constant<int, 1>(), std::true_type());
+    else go(std::integral_constant<int, 1>(), std::false_type());
+  }
+  if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
+  const int vec = vec_class(reinterpret_cast<uintptr_t>(d->tokens), reinterpret_cast<uintptr_t>(d->permuted_tokens),
+                            p.stride, p.row_bytes, p.row_bytes);
+  const unsigned blocks = static_cast<unsigned>((p.N + 3) / 4);
+  const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
+  uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
+  if (!record_event(d->ev_copy_begin, s)) return FFNWB_ERR_RUNTIME;
+  if (vec == 16)
+    hipLaunchKernelGGL(permute_rows_kernel<16>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
+                       p.N, out);
+  else if (vec == 4)
+    hipLaunchKernelGGL(permute_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
+                       p.N, out);
+  else
+    hipLaunchKernelGGL(permute_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
+                       p.N, out);
+  if (!record_event(d->ev_copy_end, s)) return FFNWB_ERR_RUNTIME;
+  return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+}
+
+}  // namespace ffnwb

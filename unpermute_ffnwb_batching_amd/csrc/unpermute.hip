@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "internal.hpp"
+#include "map_tiles.hpp"
 #include "range_order.hpp"
 #include "reduce_kernels.hpp"
 #include "sort_engine.hpp"
@@ -92,18 +93,6 @@ __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __rest
 //                            the columns) and its own tile prefix, then the start of each
 //                            of its row groups, and places its entries in row order.
 // No scan launch: the histogram is small enough for every workgroup to read it.
-constexpr int kMaskRows = 256;
-constexpr int kMaskGroupRows = 16;
-constexpr int kMaskGroups = kMaskRows / kMaskGroupRows;
-constexpr int kMaskLdsHist = 16384;    // histogram words a compaction workgroup holds
-constexpr int kMaskFusedMaxExperts = 1024;
-
-template <int W>
-__device__ __forceinline__ uint32_t load_map_unit(const uint8_t* p) {
-  if (W == 4) return *reinterpret_cast<const uint32_t*>(p);
-  return *p;
-}
-
 template <int W, typename P>
 struct ProbUnit {
   P v[W];
@@ -121,43 +110,6 @@ struct ProbUnit {
     }
   }
 };
-
-// Loads the map units of one work item (rows clamped to the map) and counts its
-// non-zero entries per column.
-template <int W>
-__device__ __forceinline__ void mask_item_counts(const uint8_t* __restrict__ map, int64_t T, int32_t E, int64_t r0,
-                                                 int c, uint32_t (&x)[kMaskGroupRows], uint32_t (&cnt)[W]) {
-#pragma unroll
-  for (int r = 0; r < kMaskGroupRows; ++r) x[r] = load_map_unit<W>(map + min(r0 + r, T - 1) * E + c * W);
-#pragma unroll
-  for (int w = 0; w < W; ++w) cnt[w] = 0u;
-#pragma unroll
-  for (int r = 0; r < kMaskGroupRows; ++r) {
-#pragma unroll
-    for (int w = 0; w < W; ++w) cnt[w] += (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
-  }
-}
-
-template <int W>
-__global__ __launch_bounds__(256) void mask_tile_count_kernel(const uint8_t* __restrict__ map, int64_t T, int32_t E,
-                                                              uint32_t* __restrict__ hist) {
-  extern __shared__ uint32_t colc[];  // [E]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) colc[e] = 0u;
-  __syncthreads();
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskRows;
-  const int cu = E / W;
-  for (int it = threadIdx.x; it < kMaskGroups * cu; it += blockDim.x) {
-    const int g = it / cu;
-    const int c = it - g * cu;
-    uint32_t x[kMaskGroupRows], cnt[W];
-    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
-#pragma unroll
-    for (int w = 0; w < W; ++w)
-      if (cnt[w] != 0) atomicAdd(&colc[c * W + w], cnt[w]);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = colc[e];
-}
 
 // LDS words of mask_compact_kernel.
 inline size_t mask_compact_lds_words(int ntiles, int E) {
