@@ -94,6 +94,70 @@ def padded_bytes(c):
     return 4 * N + nval * pelt + nval * H * elt + T * H * elt + N * pelt + 8 * N
 
 
+def permute_bytes(c, ref_nnz):
+    """Forward permute: the map, each token row once, every output row, the indices."""
+    elt = {0: 2, 1: 2, 2: 1, 3: 4}[c["dtype"]]
+    return c["T"] * c["E"] + c["T"] * c["H"] * elt + c["N"] * c["H"] * elt + 4 * c["N"]
+
+
+def measure_permute(args, stream):
+    """The forward permute (a widening of the path) at the non-padded workload's shape:
+    flushed-cache medians, the row-copy kernel's steady-state time from fence-free HIP
+    events, and (with the CPU leg) parity with the oracle."""
+    import torch
+    import synth
+    from _gpu import prepare_permute, fetch_permute
+    from unpermute_ffnwb_batching_amd.hip_events import HipEvent
+    c = synth.permute_config()
+    call = prepare_permute(c)
+    for _ in range(3):
+        call.run(stream)
+    torch.cuda.synchronize()
+    alg = permute_bytes(c, None)
+    K = max(args.steps, 5)
+    ev = [(HipEvent(), HipEvent()) for _ in range(K)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(K):
+        call.set_copy_events(*ev[i])
+        call.run(stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = s0.elapsed_time(s1) / K
+    copy_ms = float(np.mean([b.elapsed_ms(e) for b, e in ev]))
+    call.set_copy_events(None, None)
+    res = {"shape": "T=16384 topK=8 E=128 H=4096 bf16, 8 uniform experts per token",
+           "alg_bytes": alg, "us_per_call": round(call_ms * 1e3, 2), "GBps": round(alg / call_ms / 1e6, 1),
+           "copy_kernel_us": round(copy_ms * 1e3, 2),
+           "copy_kernel_GBps": round((alg - c["T"] * c["E"]) / copy_ms / 1e6, 1)}
+    if args.detail_iters > 0:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        ts = []
+        for _ in range(args.detail_iters):
+            flush.fill_(1)
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            call.run(stream)
+            e.record(stream)
+            e.synchronize()
+            ts.append(b.elapsed_time(e))
+        del flush
+        res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
+    if not args.no_cpu_baseline:
+        from _gpu import oracle_permute, check_permute
+        t1 = time.perf_counter()
+        ref = oracle_permute(c)
+        res["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+        res["cpu_oracle_GBps"] = round(alg / res["cpu_oracle_s"] / 1e9, 4)
+        try:
+            check_permute(c, fetch_permute(call), ref)
+            res["parity"] = True
+        except AssertionError as ex:
+            res["parity"] = False
+            print(f"# parity FAILED for the permute: {ex}", file=sys.stderr, flush=True)
+    return res
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in REDUCE_SOURCES:
@@ -277,6 +341,10 @@ def main():
                 "kernel": "unpermute_reduce_kernel (non-padded, BF16 rows, FP32 weights)",
                 "alg_bytes_per_launch": red_bytes, "avg_launch_us": round(hot_ms * 1e3, 2)}
 
+    next_rows = None
+    if not args.only or "permute" in args.only.split(","):
+        next_rows = {"moe_permute_nonpadded": measure_permute(args, stream)}
+
     value = step_bytes / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -287,6 +355,7 @@ def main():
                    "step_alg_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
                    "element_types": "bf16/int8 rows moved; fp32 accumulation in unpermute"},
         "roofline": roof, "cpu_baseline": cpu, "configs": detail, "parity": parity,
+        "next_rows": next_rows,
     }
     print(json.dumps(line), flush=True)
 
