@@ -18,8 +18,10 @@
 //      slots are its entries in ascending expert order: each row of the tile is walked
 //      once more, and slot k takes the row of the k-th entry, whose offset inside the tile
 //      was kept in LDS (one byte per row and expert);
-//   3. permute_rows_kernel: one wavefront per output row copies its source token row, or
-//      writes zeros.
+//   3. non-padded: permute_scatter_kernel reads each token row once and writes it to every
+//      row its slots list, and fills the rows no slot lists (zero rows past the non-zero
+//      entries, rows of experts beyond a token's topK); padded: permute_rows_kernel, one
+//      wavefront per output row copying its source token row or writing zeros.
 #include <stdio.h>
 
 #include "internal.hpp"
@@ -163,7 +165,11 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
           if (((x[u] >> (8 * w)) & 0xffu) != 0) {
             const int e = (c0 + u) * W + w;
             const uint32_t r = base[e] + inoff[rr * E + e];
-            if (k < K) sorted_indices[t * K + k] = (r < static_cast<uint64_t>(N)) ? static_cast<int32_t>(r) : -1;
+            if (k < K) {
+              sorted_indices[t * K + k] = (r < static_cast<uint64_t>(N)) ? static_cast<int32_t>(r) : -1;
+            } else if (r < static_cast<uint64_t>(N)) {
+              source_of[r] = -static_cast<int32_t>(t) - 2;  // a row no slot lists (token beyond topK)
+            }
             ++k;
           }
         }
@@ -176,20 +182,9 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
     if (r >= filled) source_of[r] = -1;
 }
 
-// One wavefront per output row: the source token's row, or zeros.
+// Writes zeros over one row (one wavefront).
 template <int VEC>
-__global__ __launch_bounds__(256) void permute_rows_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
-                                                           int64_t row_bytes, const int32_t* __restrict__ source_of,
-                                                           int64_t N, uint8_t* __restrict__ out) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
-  if (r >= N) return;
-  const int32_t src = uniform(source_of[r]);
-  const uint32_t lane = lane_id();
-  uint8_t* dst = out + r * row_bytes;
-  if (src >= 0) {
-    copy_row<VEC>(tokens + static_cast<int64_t>(src) * stride, dst, row_bytes, lane);
-    return;
-  }
+__device__ __forceinline__ void zero_row(uint8_t* __restrict__ dst, int64_t row_bytes, uint32_t lane) {
   if (VEC == 1) {
     for (int64_t i = lane; i < row_bytes; i += kWave) dst[i] = 0;
     return;
@@ -203,6 +198,92 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint8_t* __rest
     const int64_t tail = (row_bytes & 15) >> 2;
     if (lane < tail) reinterpret_cast<uint32_t*>(dst + n16 * 16)[lane] = 0u;
   }
+}
+
+// Non-padded row moves.  Workgroups below token_blocks: one wavefront per token loads
+// each 16 KiB piece of the token's row once and stores it to every row its slots list
+// (sorted_indices[t*K .. t*K+K), -1 = none).  The rest: one wavefront per 64 output rows
+// handles the rows no slot lists: source_of[r] = -1 (zeros) or -(t+2) (token t).
+template <int VEC>
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
+                                                              int64_t row_bytes,
+                                                              const int32_t* __restrict__ sorted_indices, int64_t T,
+                                                              int32_t K, const int32_t* __restrict__ source_of,
+                                                              int64_t N, unsigned token_blocks,
+                                                              uint8_t* __restrict__ out) {
+  const uint32_t lane = lane_id();
+  const int wv = uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (blockIdx.x < token_blocks) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+    if (t >= T) return;
+    const uint8_t* src = tokens + t * stride;
+    const int64_t n16 = row_bytes >> 4;
+    for (int k0 = 0; k0 < K; k0 += kWave) {
+      const int32_t d = (k0 + static_cast<int>(lane) < K) ? sorted_indices[t * K + k0 + lane] : -1;
+      const uint64_t m = wave_ballot(d >= 0);
+      if (m == 0) continue;
+      if (VEC == 1) {
+        uint64_t mm = m;
+        while (mm != 0) {
+          const int l = static_cast<int>(__builtin_ctzll(mm));
+          mm &= mm - 1;
+          const int64_t r = __builtin_amdgcn_readlane(d, l);
+          copy_row<1>(src, out + r * row_bytes, row_bytes, lane);
+        }
+        continue;
+      }
+      for (int64_t b = 0; b < n16; b += kWave * kPiece) {
+        RowPiece<VEC> piece;
+        piece.load(src, n16, b, lane);
+        uint64_t mm = m;
+        while (mm != 0) {
+          const int l = static_cast<int>(__builtin_ctzll(mm));
+          mm &= mm - 1;
+          const int64_t r = __builtin_amdgcn_readlane(d, l);
+          piece.store(out + r * row_bytes, n16, b, lane);
+        }
+      }
+      if (VEC == 4) {
+        const int64_t tail = (row_bytes & 15) >> 2;
+        uint32_t v = 0;
+        if (lane < tail) v = reinterpret_cast<const uint32_t*>(src + n16 * 16)[lane];
+        uint64_t mm = m;
+        while (mm != 0) {
+          const int l = static_cast<int>(__builtin_ctzll(mm));
+          mm &= mm - 1;
+          const int64_t r = __builtin_amdgcn_readlane(d, l);
+          if (lane < tail) reinterpret_cast<uint32_t*>(out + r * row_bytes + n16 * 16)[lane] = v;
+        }
+      }
+    }
+    return;
+  }
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x - token_blocks) * 4 + wv) * kWave;
+  const int64_t r = r0 + lane;
+  const int32_t v = (r < N) ? source_of[r] : 0;
+  uint64_t m = wave_ballot(r < N && v < 0);
+  while (m != 0) {
+    const int l = static_cast<int>(__builtin_ctzll(m));
+    m &= m - 1;
+    const int32_t vl = __builtin_amdgcn_readlane(v, l);
+    uint8_t* dst = out + (r0 + l) * row_bytes;
+    if (vl == -1) zero_row<VEC>(dst, row_bytes, lane);
+    else copy_row<VEC>(tokens + static_cast<int64_t>(-vl - 2) * stride, dst, row_bytes, lane);
+  }
+}
+
+// One wavefront per output row: the source token's row, or zeros.
+template <int VEC>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
+                                                           int64_t row_bytes, const int32_t* __restrict__ source_of,
+                                                           int64_t N, uint8_t* __restrict__ out) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (r >= N) return;
+  const int32_t src = uniform(source_of[r]);
+  const uint32_t lane = lane_id();
+  uint8_t* dst = out + r * row_bytes;
+  if (src >= 0) copy_row<VEC>(tokens + static_cast<int64_t>(src) * stride, dst, row_bytes, lane);
+  else zero_row<VEC>(dst, row_bytes, lane);
 }
 
 static int element_bytes(int dtype) {
@@ -286,7 +367,20 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
   uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
   if (!record_event(d->ev_copy_begin, s)) return FFNWB_ERR_RUNTIME;
-  if (vec == 16)
+  if (!p.padded) {
+    const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
+    const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
+    const int32_t K = static_cast<int32_t>(p.K);
+    if (vec == 16)
+      hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
+                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
+    else if (vec == 4)
+      hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
+                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
+    else
+      hipLaunchKernelGGL(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
+                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
+  } else if (vec == 16)
     hipLaunchKernelGGL(permute_rows_kernel<16>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
                        p.N, out);
   else if (vec == 4)
