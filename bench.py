@@ -100,6 +100,75 @@ def permute_bytes(c, ref_nnz):
     return c["T"] * c["E"] + c["T"] * c["H"] * elt + c["N"] * c["H"] * elt + 4 * c["N"]
 
 
+def padded_skip_bytes(c):
+    """Padded unpermute with the zero-weight skip: as padded_bytes, but only the rows whose
+    weight is non-zero are read (every valid entry's weight still is)."""
+    T, H = c["restore_shape"]
+    sI = c["sorted_indices"]
+    N = sI.size
+    E = c["probs"].shape[1]
+    elt = 4 if c["dtype"] == 3 else 2
+    pelt = 4 if c["probs_dtype"] == 3 else 2
+    ok = (sI >= 0) & (sI < T)
+    i = np.nonzero(ok)[0]
+    p = c["probs"]
+    if c["probs_dtype"] == 1:      # BF16 bits: widen to FP32
+        p = (p.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    w = p.astype(np.float32)[sI[i], i // (N // E)]
+    nval, nread = int(ok.sum()), int((w != 0).sum())
+    return 4 * N + nval * pelt + nread * H * elt + T * H * elt + N * pelt + 8 * N, nread
+
+
+def measure_skip(args, stream, c):
+    """The padded workload with the opt-in zero-weight skip: the rows whose weight is zero
+    are not read.  Flushed-cache median and steady-state time; parity with the oracle
+    run with the same option."""
+    import torch
+    from _gpu import prepare_unpermute, fetch_unpermute
+    call = prepare_unpermute(c, skip_zero_weight=True)
+    for _ in range(3):
+        call.run(stream)
+    torch.cuda.synchronize()
+    alg, nread = padded_skip_bytes(c)
+    K = max(args.steps, 5)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(K):
+        call.run(stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = s0.elapsed_time(s1) / K
+    nval = int(((c["sorted_indices"] >= 0) & (c["sorted_indices"] < c["restore_shape"][0])).sum())
+    res = {"shape": "padded E=64 C=512 T=8192 H=5120 fp16, skip_zero_weight=1",
+           "rows_valid": nval, "rows_read": nread, "alg_bytes": alg,
+           "us_per_call": round(call_ms * 1e3, 2), "GBps": round(alg / call_ms / 1e6, 1)}
+    if args.detail_iters > 0:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        ts = []
+        for _ in range(args.detail_iters):
+            flush.fill_(1)
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            call.run(stream)
+            e.record(stream)
+            e.synchronize()
+            ts.append(b.elapsed_time(e))
+        del flush
+        res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
+    if not args.no_cpu_baseline:
+        from _gpu import oracle_unpermute, check_unpermute
+        t1 = time.perf_counter()
+        ref = oracle_unpermute(c, skip_zero_weight=True)
+        res["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+        try:
+            check_unpermute(c, fetch_unpermute(call, c), ref)
+            res["parity"] = True
+        except AssertionError as ex:
+            res["parity"] = False
+            print(f"# parity FAILED for the skip: {ex}", file=sys.stderr, flush=True)
+    return res
+
+
 def measure_permute(args, stream):
     """The forward permute (a widening of the path) at the non-padded workload's shape:
     flushed-cache medians, the row-copy kernel's steady-state time from fence-free HIP
@@ -341,9 +410,12 @@ def main():
                 "kernel": "unpermute_reduce_kernel (non-padded, BF16 rows, FP32 weights)",
                 "alg_bytes_per_launch": red_bytes, "avg_launch_us": round(hot_ms * 1e3, 2)}
 
-    next_rows = None
+    next_rows = {}
     if not args.only or "permute" in args.only.split(","):
-        next_rows = {"moe_permute_nonpadded": measure_permute(args, stream)}
+        next_rows["moe_permute_nonpadded"] = measure_permute(args, stream)
+    if "unpermute_padded" in cases:
+        next_rows["unpermute_padded_skip_zero_weight"] = measure_skip(args, stream, cases["unpermute_padded"])
+    next_rows = next_rows or None
 
     value = step_bytes / (ms * 1e-3) / 1e9
     line = {

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FFNWB_ABI_VERSION 2
+#define FFNWB_ABI_VERSION 3
 
 /* Status codes.  The first three take the aclnn values both pages list. */
 #define FFNWB_OK                 0
@@ -179,6 +179,14 @@ typedef struct moe_unpermute_desc {
      the gather-reduce kernel.  NULL = not recorded. */
   void* ev_reduce_begin;
   void* ev_reduce_end;
+
+  /* Opt-in (with probs): leave out every term whose weight is 0 instead of adding
+     0 * row -- the article's kernel copies a slot's row only when its prob is non-zero
+     ("Kernel implementation").  The result is the same for finite rows; a zero-weight
+     row holding inf or NaN no longer reaches the output; zero-weight rows are not read.
+     Applied in both layouts.  0 = off (formula-faithful, the default). */
+  int32_t skip_zero_weight;
+  int32_t reserved0;        /* must be 0 */
 } moe_unpermute_desc;
 
 /* Validates *d and returns the workspace size in bytes (host only, no device work).

@@ -36,13 +36,19 @@ Readings taken where the article is silent, garbled or self-contradictory
     (outside [0, rows)) first, and permuteTokenId = outIndex // topK -- the
     only reading that fits the documented value ranges of both outputs
     ("parity unpinned" beyond ranges, permutation and stability);
-  * zero weights are multiplied in, not skipped.
+  * zero weights are multiplied in, not skipped, unless ``skip_zero_weight`` is set:
+    then, as the article's kernel description has it (each slot's row is copied only
+    when its index is valid and its prob is non-zero), terms with weight 0 are left
+    out -- the same result for finite rows, different where a zero-weight row holds
+    inf or NaN.  The skip is applied in both layouts.
 
 Pins (tests/test_oracle_unpermute.py): the article's padded {2,2} example
 (formula result; the article's printed "all 2" claim contradicts its own
 formula), closed forms (permute-then-unpermute identities, softmax-weighted
 recombination), brute force against torch index_add_ in float64 within the FP32
-error bound, and property checks of the auxiliary outputs.
+error bound, property checks of the auxiliary outputs, and for the zero-weight
+skip: equality with the formula on finite rows and two worked examples where a
+zero-weight row holds NaN / inf.
 """
 
 import numpy as np
@@ -52,7 +58,8 @@ from .numerics import to_f32, from_f32, storage_dtype
 
 def moe_token_unpermute_with_routing_map(permuted_tokens, tokens_dtype, sorted_indices,
                                          padded_mode, restore_shape, routing_map=None,
-                                         probs=None, probs_dtype=None, weight_index=0):
+                                         probs=None, probs_dtype=None, weight_index=0,
+                                         skip_zero_weight=False):
     """Reference unpermute.
 
     permuted_tokens : [rows, H] stored as ``tokens_dtype`` (see numerics).
@@ -100,6 +107,8 @@ def moe_token_unpermute_with_routing_map(permuted_tokens, tokens_dtype, sorted_i
             if not (0 <= t < T):
                 continue
             if has_probs:
+                if skip_zero_weight and w[r] == 0:
+                    continue  # the kernel copies a row only when its prob is non-zero
                 acc[t] = acc[t] + x[r] * w[r]
             else:
                 acc[t] = acc[t] + x[r]
@@ -123,6 +132,8 @@ def moe_token_unpermute_with_routing_map(permuted_tokens, tokens_dtype, sorted_i
                     continue  # -1 (or any out-of-range index) marks an empty slot
                 if has_probs:
                     w = P[r] if weight_index == 0 else P[i]
+                    if skip_zero_weight and w == 0:
+                        continue  # the kernel copies a row only when its prob is non-zero
                     acc[t] = acc[t] + x[r] * w
                 else:
                     acc[t] = acc[t] + x[r]

@@ -112,15 +112,15 @@ def from_torch_elems(t, dt):
     return a.numpy()
 
 
-def oracle_unpermute(case, weight_index=0):
+def oracle_unpermute(case, weight_index=0, skip_zero_weight=False):
     from oracle import moe_token_unpermute_with_routing_map
     return moe_token_unpermute_with_routing_map(
         case["permuted"], case["dtype"], case["sorted_indices"], case["padded_mode"], case["restore_shape"],
         routing_map=case["routing_map"], probs=case["probs"], probs_dtype=case["probs_dtype"],
-        weight_index=weight_index)
+        weight_index=weight_index, skip_zero_weight=skip_zero_weight)
 
 
-def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None):
+def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None, skip_zero_weight=False):
     T, H = case["restore_shape"]
     N = case["sorted_indices"].shape[0]
     x = to_torch_elems(case["permuted"], case["dtype"])
@@ -133,7 +133,8 @@ def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None):
     if probs is not None:
         out["permute_probs"] = _canary((N,), probs.dtype)
     return F.UnpermuteCall(x, dev(case["sorted_indices"]), rmap, probs, padded_mode=case["padded_mode"],
-                           restore_shape=(T, H), weight_index=weight_index, aux=aux, out=out, ev_reduce=ev_reduce)
+                           restore_shape=(T, H), weight_index=weight_index, aux=aux, out=out, ev_reduce=ev_reduce,
+                           skip_zero_weight=skip_zero_weight)
 
 
 def fetch_unpermute(call, case):
@@ -147,8 +148,8 @@ def fetch_unpermute(call, case):
     return r
 
 
-def run_unpermute(case, weight_index=0, aux=True):
-    call = prepare_unpermute(case, weight_index, aux)
+def run_unpermute(case, weight_index=0, aux=True, skip_zero_weight=False):
+    call = prepare_unpermute(case, weight_index, aux, skip_zero_weight=skip_zero_weight)
     call.run()
     torch.cuda.synchronize()
     return fetch_unpermute(call, case)

@@ -39,7 +39,7 @@ def test_descriptor_layout_and_version():
     assert L.ffnwb_batching_desc_size() == ctypes.sizeof(F.BatchingDesc)
     assert L.moe_unpermute_desc_size() == ctypes.sizeof(F.UnpermuteDesc)
     assert L.moe_permute_desc_size() == ctypes.sizeof(F.PermuteDesc)
-    assert F.ffnwb_abi_version() == 2
+    assert F.ffnwb_abi_version() == 3
     for st in (0, 161001, 161002, 561103, 1, 2):
         assert F.ffnwb_status_string(st).startswith("FFNWB_")
 
@@ -167,7 +167,7 @@ def test_unpermute_optional_outputs_may_be_null():
     dict(dtype=2), dict(dtype=7), dict(dtype=0, probs_dtype=3), dict(dtype=3, probs_dtype=1),
     dict(dtype=1, probs_dtype=0), dict(routing_map=None), dict(padded_mode=2), dict(weight_index=2),
     dict(hidden=0), dict(num_rows=63), dict(num_indices=65, num_rows=65), dict(num_tokens=-1),
-    dict(num_tokens=0), dict(padded_mode=1, num_experts=5),
+    dict(num_tokens=0), dict(padded_mode=1, num_experts=5), dict(skip_zero_weight=2), dict(reserved0=1),
 ])
 def test_unpermute_invalid_parameters(over):
     assert _uws(_unpermute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID

@@ -143,3 +143,60 @@ def test_nondefault_streams_and_back_to_back_calls():
     torch.cuda.synchronize()
     for c, call, ref in zip(cases, calls, refs):
         check_unpermute(c, fetch_unpermute(call, c), ref)
+
+
+# ----------------------------------------------------------------------------- zero-weight skip
+
+SKIP = [
+    ("padded", dict(E=16, C=64, T=1000, H=512, dtype=synth.FP16, probs_dtype=synth.FP16)),
+    ("padded", dict(E=8, C=40, T=300, H=24, dtype=synth.BF16, probs_dtype=synth.FP32)),
+    ("padded", dict(E=4, C=33, T=200, H=21, dtype=synth.FP32, probs_dtype=synth.FP32)),   # element path
+    ("nonpadded", dict(T=400, K=4, E=32, H=256, dtype=synth.BF16, probs_dtype=synth.FP32, n_empty=300,
+                       rows_mode="slots")),                                             # rows past nnz weigh 0
+]
+
+
+def _skip_case(kind, kw, seed):
+    if kind == "padded":
+        return synth.unpermute_padded_case(seed, **kw)
+    return synth.unpermute_nonpadded_case(seed, **kw)
+
+
+@pytest.mark.parametrize("poison", [False, True])
+@pytest.mark.parametrize("params", SKIP, ids=[str(i) for i in range(len(SKIP))])
+def test_zero_weight_skip(params, poison):
+    kind, kw = params
+    case = _skip_case(kind, kw, 61 + len(kw))
+    # zero a third of the probs (half of those as -0.0) so that routed entries weigh 0
+    rng = np.random.default_rng(62)
+    pr = case["probs"].copy()
+    bits = pr.view(np.uint32 if pr.itemsize == 4 else np.uint16)
+    pick = rng.random(pr.shape) < 1 / 3
+    neg = rng.random(pr.shape) < 0.5
+    bits[pick] = 0
+    bits[pick & neg] = 0x80000000 if pr.itemsize == 4 else 0x8000
+    case = dict(case, probs=pr)
+    if poison:
+        # NaN in every permuted row whose weight is 0: the skip must keep them out
+        ref0 = oracle_unpermute(case)
+        from oracle import numerics as nm
+        w = nm.to_f32(ref0["permute_probs"], case["probs_dtype"])
+        zero_rows = np.nonzero(w == 0)[0] if kind == "padded" else \
+            np.array([r for r in range(len(w)) if w[r] == 0], np.int64)
+        nan_bits = {synth.FP16: np.float16("nan"), synth.FP32: np.float32("nan")}
+        x = case["permuted"].copy()
+        if case["dtype"] == synth.BF16:
+            x[zero_rows] = np.uint16(0x7fc0)
+        else:
+            x[zero_rows] = nan_bits[case["dtype"]]
+        case = dict(case, permuted=x)
+    print(f"unpermute skip {kind} {kw} poison={poison}", flush=True)
+    ref = oracle_unpermute(case, skip_zero_weight=True)
+    got = run_unpermute(case, skip_zero_weight=True)
+    check_unpermute(case, got, ref)
+
+
+def test_zero_weight_skip_full_size_padded():
+    case = synth.unpermute_config(5)
+    print("unpermute padded workload with the zero-weight skip", flush=True)
+    check_unpermute(case, run_unpermute(case, skip_zero_weight=True), oracle_unpermute(case, skip_zero_weight=True))

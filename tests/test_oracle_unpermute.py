@@ -273,3 +273,52 @@ def test_aux_outputs_properties(padded):
     assert (np.diff(oi)[same] > 0).all()                         # stable among equal keys
     ts = torch.sort(torch.from_numpy(key), stable=True)
     assert np.array_equal(ts.indices.numpy(), oi)
+
+
+# ------------------------------------------------------------------ opt-in zero-weight skip
+
+@pytest.mark.parametrize("padded", [False, True])
+def test_zero_weight_skip_matches_the_formula_on_finite_rows(padded):
+    # 0 * x = +-0 and acc + (+-0) = acc for any acc reachable from +0.0, so leaving the
+    # term out cannot change a finite result
+    if padded:
+        case = synth.unpermute_padded_case(41, E=8, C=16, T=40, H=12, dtype=nm.DT_BF16, probs_dtype=nm.DT_FP32)
+    else:
+        case = synth.unpermute_nonpadded_case(42, T=30, K=4, E=8, H=12, dtype=nm.DT_FP16, probs_dtype=nm.DT_FP16,
+                                              n_empty=20)
+    args = (case["permuted"], case["dtype"], case["sorted_indices"], case["padded_mode"], case["restore_shape"])
+    kw = dict(routing_map=case["routing_map"], probs=case["probs"], probs_dtype=case["probs_dtype"])
+    a = unpermute(*args, **kw)
+    b = unpermute(*args, skip_zero_weight=True, **kw)
+    assert np.array_equal(np.asarray(a["unpermuted"]).view(np.uint8), np.asarray(b["unpermuted"]).view(np.uint8))
+
+
+def test_zero_weight_skip_padded_worked_example():
+    # expert 0 holds tokens 0 and 1, expert 1 tokens 0 and 2; token 1's row has weight 0
+    # and holds NaN / inf: the skip leaves it out, the formula propagates it
+    nan, inf = np.float32("nan"), np.float32("inf")
+    x = np.array([[2, 4], [nan, inf], [8, 8], [3, 5]], np.float32)
+    sI = np.array([0, 1, 0, 2], np.int32)
+    probs = np.array([[0.5, 0.25], [0.0, 0.0], [0.0, 1.0]], np.float32)
+    rmap = (probs != 0).astype(np.int8)
+    out = unpermute(x, nm.DT_FP32, sI, True, (3, 2), routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32,
+                    skip_zero_weight=True)
+    assert out["unpermuted"].tolist() == [[3.0, 4.0], [0.0, 0.0], [3.0, 5.0]]
+    with np.errstate(invalid="ignore"):  # inf * 0
+        plain = unpermute(x, nm.DT_FP32, sI, True, (3, 2), routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32)
+    assert np.isnan(plain["unpermuted"][1]).all()
+
+
+def test_zero_weight_skip_nonpadded_worked_example():
+    # map [[1,1],[1,0]]: expert-major weights P = [p00, p10, p01, 0]; slot 3 reads row 3,
+    # whose weight is the zero padding of P
+    nan = np.float32("nan")
+    x = np.array([[2, 2], [4, 6], [6, 2], [nan, nan]], np.float32)
+    sI = np.array([0, 2, 1, 3], np.int32)
+    probs = np.array([[0.5, 0.5], [1.0, 0.0]], np.float32)
+    rmap = np.array([[1, 1], [1, 0]], np.int8)
+    out = unpermute(x, nm.DT_FP32, sI, False, (2, 2), routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32,
+                    skip_zero_weight=True)
+    assert out["unpermuted"].tolist() == [[4.0, 2.0], [4.0, 6.0]]
+    plain = unpermute(x, nm.DT_FP32, sI, False, (2, 2), routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32)
+    assert np.isnan(plain["unpermuted"][1]).all()

@@ -236,11 +236,13 @@ class UnpermuteCall:
 
     ``permuted_tokens`` [rows, H] (fp16 / bf16 / fp32), ``sorted_indices`` int32 [N],
     ``routing_map`` int8/bool [T, E] or None, ``probs`` [T, E] or None.
-    ``aux`` False skips out_index / permute_token_id.
+    ``aux`` False skips out_index / permute_token_id.  ``skip_zero_weight`` leaves out
+    terms whose weight is 0 (opt-in; see include/ffnwb.h).
     """
 
     def __init__(self, permuted_tokens, sorted_indices, routing_map=None, probs=None, *, padded_mode,
-                 restore_shape, weight_index=0, aux=True, out=None, workspace=None, ev_reduce=None):
+                 restore_shape, weight_index=0, aux=True, out=None, workspace=None, ev_reduce=None,
+                 skip_zero_weight=False):
         T, H = (int(v) for v in restore_shape)
         dev = permuted_tokens.device
         out = dict(out or {})
@@ -264,6 +266,7 @@ class UnpermuteCall:
         d.probs_dtype = _FLOAT_CODE.get(probs.dtype, -1) if probs is not None else 0
         d.padded_mode = int(bool(padded_mode))
         d.weight_index = int(weight_index)
+        d.skip_zero_weight = int(bool(skip_zero_weight))
         d.num_rows = permuted_tokens.shape[0]
         d.hidden = H if permuted_tokens.dim() < 2 else permuted_tokens.shape[1]
         d.num_tokens = T

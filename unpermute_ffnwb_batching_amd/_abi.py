@@ -2,7 +2,7 @@
 
 import ctypes
 
-FFNWB_ABI_VERSION = 2
+FFNWB_ABI_VERSION = 3
 
 FFNWB_OK = 0
 FFNWB_ERR_PARAM_NULLPTR = 161001
@@ -44,6 +44,7 @@ class UnpermuteDesc(ctypes.Structure):
         ("unpermuted_tokens", _vp), ("out_index", _vp), ("permute_token_id", _vp),
         ("permute_probs", _vp),
         ("ev_reduce_begin", _vp), ("ev_reduce_end", _vp),
+        ("skip_zero_weight", _i32), ("reserved0", _i32),
     ]
 
 

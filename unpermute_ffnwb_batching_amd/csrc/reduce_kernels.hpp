@@ -20,6 +20,7 @@ struct ReduceArgs {
   const int32_t* order;  // padded: sorted position -> permuted row (out_index)
   const void* w;         // permute_probs (weights), probs element type
   uint8_t* out;
+  int32_t skip_zero;     // with weights: leave out terms of weight 0 (their rows are not read)
 };
 
 // One workgroup per token; each thread owns CPT 16-byte chunks of the hidden dimension
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(1024) void unpermute_reduce_kernel(ReduceArgs a) {
       }
       float wl = 1.0f;
       if (kHasW && ok) wl = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : static_cast<int64_t>(r));
+      if (kHasW && a.skip_zero != 0) ok = ok && wl != 0.0f;  // uniform switch
       uint64_t vm = wave_ballot(ok);
       while (vm != 0) {
         int32_t rr[B];
@@ -139,12 +141,12 @@ __global__ __launch_bounds__(1024) void unpermute_reduce_elem_kernel(ReduceArgs 
     for (int64_t k = 0; k < nent; ++k) {
       const int64_t idx = kPadded ? a.order[ebase + k] : a.sI[ebase + k];
       if (!kPadded && !(idx >= 0 && idx < a.rows)) continue;
-      const float f = load_elem<TT>(a.x, idx * a.H + h);
       if (kHasW) {
         const float w = load_elem<TW>(a.w, MODE == kNonPadW1 ? ebase + k : idx);
-        acc = acc + f * w;
+        if (a.skip_zero != 0 && w == 0.0f) continue;
+        acc = acc + load_elem<TT>(a.x, idx * a.H + h) * w;
       } else {
-        acc = acc + f;
+        acc = acc + load_elem<TT>(a.x, idx * a.H + h);
       }
     }
     store_elem<TT>(a.out, t * a.H + h, acc);

@@ -475,6 +475,7 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
     return FFNWB_ERR_PARAM_INVALID;
   if (d->padded_mode != 0 && d->padded_mode != 1) return FFNWB_ERR_PARAM_INVALID;
   if (d->weight_index != 0 && d->weight_index != 1) return FFNWB_ERR_PARAM_INVALID;
+  if ((d->skip_zero_weight != 0 && d->skip_zero_weight != 1) || d->reserved0 != 0) return FFNWB_ERR_PARAM_INVALID;
   if (d->hidden <= 0 || d->num_tokens < 0 || d->num_indices < 0 || d->num_rows < 0) return FFNWB_ERR_PARAM_INVALID;
   if (d->num_rows != d->num_indices) return FFNWB_ERR_PARAM_INVALID;
   const int64_t lim = (int64_t{1} << 31) - 2;
@@ -618,6 +619,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
   ra.H = p.H;
   ra.T = p.T;
   ra.out = static_cast<uint8_t*>(d->unpermuted_tokens);
+  ra.skip_zero = d->skip_zero_weight;
 
   if (!p.padded) {
     // workspace regions, in the order plan_unpermute sized them
