@@ -307,3 +307,91 @@ def permute_config():
 
 def config(n):
     return batching_config(n) if n <= 3 else unpermute_config(n)
+
+
+# ----------------------------------------------------------------------------- schedule context
+
+def _ctx_dtype():
+    """The usage example's packed ScheduleContext, declared member by member (a NumPy
+    structured type without alignment padding, as the definition is packed)."""
+    r = lambda name, n: (name, "i1", (n,))
+    common = [("session_num", "<u4"), ("micro_batch_num", "<u4"), ("micro_batch_size", "<u4"),
+              ("selected_expert_num", "<u4"), ("expert_num", "<u4"), ("attn_to_ffn_token_size", "<u4"),
+              ("ffn_to_attn_token_size", "<u4"), ("schedule_mode", "<i4"), r("reserve0", 96)]
+    control = [("run_flag", "<i4"), r("reserve2", 124)]
+    ffn = [("token_info_buf", "<u8"), ("token_info_buf_size", "<u8"), ("token_data_buf", "<u8"),
+           ("token_data_buf_size", "<u8"), ("polling_index", "<u8"), r("reserve3", 88),
+           ("layer_ids_buf", "<u8"), ("layer_ids_buf_size", "<u8"), ("session_ids_buf", "<u8"),
+           ("session_ids_buf_size", "<u8"), ("micro_batch_ids_buf", "<u8"), ("micro_batch_ids_buf_size", "<u8"),
+           ("expert_ids_buf", "<u8"), ("expert_ids_buf_size", "<u8"), ("out_num", "<u4"), r("reserve4", 60)]
+    attention = [("token_info_buf", "<u8"), ("token_info_buf_size", "<u8"), ("token_data_buf", "<u8"),
+                 ("token_data_buf_size", "<u8"), ("micro_batch_id", "<u4"), r("reserve5", 92)]
+    return np.dtype([("common", common), ("control", control), ("attention", attention), ("ffn", ffn),
+                     r("reserve6", 384)])
+
+
+CTX_DTYPE = _ctx_dtype()
+
+
+def ffn_data_desc_dtype(n_ids):
+    """The usage example's packed FfnDataDesc with its trailing expert-id array sized."""
+    return np.dtype([("flag", "<i4"), ("layer_id", "<i4"), ("expert_ids", "<i4", (n_ids,))])
+
+
+def schedule_context(session_num, micro_batch_num, micro_batch_size, selected_expert_num, expert_num,
+                     token_info_buf, token_info_buf_size, token_data_buf, token_data_buf_size,
+                     polling_index=0, schedule_mode=0, run_flag=1, token_sizes=(512, 512)):
+    """The 1024 context bytes, filled like the usage example fills them."""
+    c = np.zeros((), dtype=CTX_DTYPE)
+    cm = c["common"]
+    cm["session_num"], cm["micro_batch_num"] = session_num, micro_batch_num
+    cm["micro_batch_size"], cm["selected_expert_num"] = micro_batch_size, selected_expert_num
+    cm["expert_num"] = expert_num
+    cm["attn_to_ffn_token_size"], cm["ffn_to_attn_token_size"] = token_sizes
+    cm["schedule_mode"] = schedule_mode
+    c["control"]["run_flag"] = run_flag
+    f = c["ffn"]
+    f["token_info_buf"], f["token_info_buf_size"] = token_info_buf, token_info_buf_size
+    f["token_data_buf"], f["token_data_buf_size"] = token_data_buf, token_data_buf_size
+    f["polling_index"] = polling_index
+    return np.frombuffer(c.tobytes(), dtype=np.uint8).copy()
+
+
+def schedule_area(seed, A, M, BS, K1, H, expert_num, layer_num, token_dtype, n_not_ready=0, n_bad_ids=0,
+                  bad_layers=0):
+    """The attention->FFN data area of A sessions x M micro-batches: ``info`` (the
+    FfnDataDesc of every chunk, session-major, as uint8 bytes) and ``data`` (uint8
+    [A*M*BS*K1, row]: each chunk's BS*K1 rows in chunk order; an INT8 row is H bytes
+    then its FP32 scale).  ``n_not_ready`` chunks get a flag other than 1; ids uniform
+    within the layer, ``n_bad_ids`` of them out of range; ``bad_layers`` chunks get an
+    out-of-range layer id."""
+    rng = np.random.default_rng(seed)
+    nch, n = A * M, BS * K1
+    L = max(layer_num, 1)
+    per_layer = expert_num // L
+    row = H * _ELT[token_dtype] + (4 if token_dtype == INT8 else 0)
+    rows = nch * n
+    if token_dtype == INT8:
+        data = np.empty((rows, row), dtype=np.uint8)
+        data[:, :H] = rng.integers(-127, 128, size=(rows, H), dtype=np.int16).astype(np.int8).view(np.uint8)
+        data[:, H:] = rng.uniform(1e-3, 1e-1, size=rows).astype(np.float32).view(np.uint8).reshape(rows, 4)
+    else:
+        data = _normal_elements(rng, (rows, H), token_dtype).view(np.uint8).reshape(rows, row)
+    flags = np.ones(nch, dtype=np.int32)
+    if n_not_ready:
+        flags[rng.choice(nch, size=n_not_ready, replace=False)] = rng.choice(
+            np.array([0, 2, -1], dtype=np.int32), size=n_not_ready)
+    layers = rng.integers(0, L, size=nch).astype(np.int32)
+    if bad_layers:
+        layers[rng.choice(nch, size=bad_layers, replace=False)] = L
+    ids = rng.integers(0, per_layer, size=(nch, n)).astype(np.int32)
+    if n_bad_ids:
+        flat = ids.reshape(-1)
+        bad = rng.choice(flat.size, size=n_bad_ids, replace=False)
+        flat[bad] = rng.choice(np.array([-1, per_layer, per_layer + 9, 1 << 30], dtype=np.int32), size=n_bad_ids)
+    desc = np.zeros(nch, dtype=ffn_data_desc_dtype(n))
+    desc["flag"], desc["layer_id"], desc["expert_ids"] = flags, layers, ids
+    info = np.frombuffer(desc.tobytes(), dtype=np.uint8).copy()
+    return dict(info=info, data=data, flags=flags, layers=layers, expert_ids=ids, row=row,
+                A=A, M=M, BS=BS, K1=K1, H=H, expert_num=expert_num, layer_num=layer_num,
+                token_dtype=token_dtype)
