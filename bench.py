@@ -169,6 +169,66 @@ def measure_skip(args, stream, c):
     return res
 
 
+def ctx_bytes(area, actual):
+    """Batching from a ScheduleContext: the context words read, the chosen chunks'
+    descriptors, the moved rows (read and written), the per-row ids and group_list."""
+    A, n, E = area["A"], area["BS"] * area["K1"], area["expert_num"]
+    row = area["row"] - (4 if area["token_dtype"] == 2 else 0)
+    return 424 + A * (8 + 4 * n) + actual * (2 * row + 16 + (8 if area["token_dtype"] == 2 else 0)) + 16 * E + 8
+
+
+def measure_ctx(args, stream):
+    """Batching fed by a ScheduleContext at the BF16 batching workload's shape: A=16
+    sessions x 4 micro-batches of BS=32, K+1=9 slots, H=7168 BF16 rows, 256 experts;
+    the call batches micro-batch 3 with needSchedule=1 (every flag read, all ready)."""
+    import torch
+    import synth
+    from _gpu import prepare_ctx, fetch_batching
+    area = synth.schedule_area(13, 16, 4, 32, 9, 7168, 256, 1, synth.BF16)
+    call = prepare_ctx(area, 3, 1)
+    for _ in range(3):
+        call.run(stream)
+    torch.cuda.synchronize()
+    actual = int(call.out["actual_token_num"].item())
+    alg = ctx_bytes(area, actual)
+    K = max(args.steps, 5)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(K):
+        call.run(stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = s0.elapsed_time(s1) / K
+    res = {"shape": "A=16 M=4 BS=32 K+1=9 H=7168 bf16, 256 experts, micro-batch 3, needSchedule=1",
+           "rows": actual, "alg_bytes": alg, "us_per_call": round(call_ms * 1e3, 2),
+           "GBps": round(alg / call_ms / 1e6, 1)}
+    if args.detail_iters > 0:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        ts = []
+        for _ in range(args.detail_iters):
+            flush.fill_(1)
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            call.run(stream)
+            e.record(stream)
+            e.synchronize()
+            ts.append(b.elapsed_time(e))
+        del flush
+        res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
+    if not args.no_cpu_baseline:
+        from _gpu import oracle_ctx, check_ctx
+        t1 = time.perf_counter()
+        ref = oracle_ctx(area, call)
+        res["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+        try:
+            check_ctx(area, call, fetch_batching(call), ref)
+            res["parity"] = True
+        except AssertionError as ex:
+            res["parity"] = False
+            print(f"# parity FAILED for the context batching: {ex}", file=sys.stderr, flush=True)
+    return res
+
+
 def measure_permute(args, stream):
     """The forward permute (a widening of the path) at the non-padded workload's shape:
     flushed-cache medians, the row-copy kernel's steady-state time from fence-free HIP
@@ -413,6 +473,8 @@ def main():
     next_rows = {}
     if not args.only or "permute" in args.only.split(","):
         next_rows["moe_permute_nonpadded"] = measure_permute(args, stream)
+    if not args.only or "context" in args.only.split(","):
+        next_rows["batching_from_context"] = measure_ctx(args, stream)
     if "unpermute_padded" in cases:
         next_rows["unpermute_padded_skip_zero_weight"] = measure_skip(args, stream, cases["unpermute_padded"])
     next_rows = next_rows or None

@@ -15,6 +15,11 @@
  *                      branches: padded x has-probs), "Parameters",
  *                      "Supplementary notes", "Constraints", "Return values
  *                      and error codes".
+ *   ffnwb_batching_ctx -- the same batching, fed the way the API page's own interface
+ *                      feeds it: a 1024-byte ScheduleContext whose FfnArea points at
+ *                      the attention->FFN data area ("Function description" step 1,
+ *                      the scheduleContext / needSchedule rows of the parameter table,
+ *                      the usage example's packed struct definitions).
  *   moe_permute     -- the forward permute the same article names in "Operator
  *                      positioning"; its outputs are the arrangement the
  *                      unpermute's formulas invert (see its section below).
@@ -47,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FFNWB_ABI_VERSION 3
+#define FFNWB_ABI_VERSION 4
 
 /* Status codes.  The first three take the aclnn values both pages list. */
 #define FFNWB_OK                 0
@@ -130,6 +135,83 @@ int ffnwb_batching_workspace_size(const ffnwb_batching_desc* d, size_t* ws_bytes
 /* Validates again, then enqueues the batching on `stream`.  `workspace` must hold at
    least the queried size (FFNWB_ERR_WORKSPACE otherwise; NULL allowed when it is 0). */
 int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * FFN-worker batching from a ScheduleContext (aclnnFfnWorkerBatching API page:
+ * "Function description" step 1; the scheduleContext, needSchedule and maxOutShape rows
+ * of the parameter table; the usage example's packed ScheduleContext and FfnDataDesc).
+ *
+ * schedule_context points at the 1024-byte context in device memory.  The library reads
+ * it on the device only (no host copy, no synchronisation), at the offsets of the packed
+ * definition: CommonArea at 0 (u32 session_num, micro_batch_num, micro_batch_size,
+ * selected_expert_num, expert_num at 0, 4, 8, 12, 16), FfnArea at 384 (u64
+ * token_info_buf, token_info_buf_size, token_data_buf, token_data_buf_size,
+ * polling_index at +0, +8, +16, +24, +32).  The two FfnArea buffers are device memory.
+ *
+ * Data area, with M = micro_batch_num and n = BS*K1: chunk (session s, micro-batch m)
+ * is chunk number s*M + m.  Its FfnDataDesc -- int32 flag, int32 layer_id, int32
+ * expert_ids[n] -- starts at byte (s*M + m) * (8 + 4n) of token_info; its n rows start at
+ * row (s*M + m) * n of token_data, rows back to back, each H elements (INT8: H bytes then
+ * the FP32 dynamic scale).
+ *
+ * One call batches micro-batch m = polling_index of every session: slot s*n + j is entry
+ * j of session s's chunk.  need_schedule = 1: a chunk whose flag is not 1 takes no part
+ * (its slots count as masked; each flag is read once with an acquire load, nothing
+ * waits).  need_schedule = 0: flags are not read.  From there the results are those of
+ * ffnwb_batching on the flattened slots, with session id s, micro-batch id m and token
+ * id s*n + j.
+ *
+ * The context must agree with the call: session_num = A, micro_batch_size = BS,
+ * selected_expert_num = K1, expert_num * max(layer_num, 1) = the descriptor's
+ * expert_num, 1 <= micro_batch_num <= 64, polling_index < micro_batch_num, both buffer
+ * pointers non-NULL, token_info 4-byte and token_data 16-byte aligned, token_info at
+ * least A*M*(8 + 4n) bytes and token_data at least A*M*n rows.  Otherwise nothing is read
+ * from the data area, actual_token_num = 0, group_list is all {0, 0}, err_count = 0, and
+ * *ctx_status holds the FFNWB_CTX_* bits of every failed check (0 when all pass).
+ * The buffer pointers must address device memory of the stated sizes: they cannot be
+ * checked beyond that.
+ * ------------------------------------------------------------------------------------------ */
+#define FFNWB_CTX_BYTES          1024
+#define FFNWB_CTX_SHAPE          1  /* session_num / micro_batch_size / selected_expert_num / expert_num */
+#define FFNWB_CTX_POLLING        2  /* micro_batch_num outside [1, 64], or polling_index >= it */
+#define FFNWB_CTX_POINTER        4  /* a data-area pointer is NULL or misaligned */
+#define FFNWB_CTX_BUFFER         8  /* a data-area buffer is smaller than the layout needs */
+
+typedef struct ffnwb_batching_ctx_desc {
+  /* maxOutShape {A, BS, topK+1, H}, expert_num, layer_num, token_dtype: as in
+     ffnwb_batching_desc. */
+  int64_t A, BS, K1, H;
+  int64_t expert_num;
+  int64_t layer_num;
+  int32_t token_dtype;
+  int32_t need_schedule;          /* 0 or 1 */
+  const void* schedule_context;   /* device pointer to FFNWB_CTX_BYTES bytes, 8-byte aligned */
+
+  /* Outputs: as in ffnwb_batching_desc, plus the context check. */
+  void* y;
+  int32_t* session_ids_out;
+  int32_t* micro_batch_ids_out;
+  int32_t* token_ids;
+  int32_t* expert_offsets;
+  float* dynamic_scale;           /* INT8 only */
+  int64_t* group_list;
+  int64_t* actual_token_num;
+  int32_t* err_count;             /* or NULL */
+  int32_t* ctx_status;            /* [1], required: 0 or FFNWB_CTX_* bits */
+
+  /* Optional timing hooks around the row-gather kernel, as in ffnwb_batching_desc. */
+  void* ev_gather_begin;
+  void* ev_gather_end;
+} ffnwb_batching_ctx_desc;
+
+/* Validates the host-side fields of *d and returns the workspace size (host only).
+   Errors: FFNWB_ERR_PARAM_NULLPTR (d, ws_bytes, schedule_context or a required output
+   NULL), FFNWB_ERR_PARAM_INVALID (need_schedule not 0 or 1, or a range of
+   ffnwb_batching_desc violated). */
+int ffnwb_batching_ctx_workspace_size(const ffnwb_batching_ctx_desc* d, size_t* ws_bytes);
+
+/* Validates again, then enqueues the context decode and the batching on `stream`. */
+int ffnwb_batching_ctx(const ffnwb_batching_ctx_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * MoE token unpermute with routing map (MoeTokenUnpermuteWithRoutingMap article).
@@ -261,6 +343,7 @@ int ffnwb_abi_version(void);
 
 /* sizeof the descriptors as compiled into the library (binding self-check). */
 size_t ffnwb_batching_desc_size(void);
+size_t ffnwb_batching_ctx_desc_size(void);
 size_t moe_unpermute_desc_size(void);
 size_t moe_permute_desc_size(void);
 

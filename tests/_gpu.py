@@ -231,3 +231,61 @@ def check_permute(case, got, ref=None):
     rb = np.ascontiguousarray(ref["permuted_tokens"]).view(np.uint8).reshape(got["permuted_tokens"].shape)
     assert np.array_equal(got["permuted_tokens"], rb), "permuted rows differ"
     return ref
+
+
+# ----------------------------------------------------------------------------- batching from a ScheduleContext
+
+def ctx_fields(area, info, data, polling):
+    """Context fields that describe ``area`` uploaded at ``info`` / ``data`` (device tensors)."""
+    L = max(area["layer_num"], 1)
+    return dict(session_num=area["A"], micro_batch_num=area["M"], micro_batch_size=area["BS"],
+                selected_expert_num=area["K1"], expert_num=area["expert_num"] // L,
+                token_info_buf=info.data_ptr(), token_info_buf_size=info.numel(),
+                token_data_buf=data.data_ptr(), token_data_buf_size=data.numel(), polling_index=polling)
+
+
+def prepare_ctx(area, polling, need_schedule, ctx_over=None, ev_gather=None, ptr_shift=None):
+    """Upload the data area and a context describing it (fields in ``ctx_over`` replaced,
+    pointer fields in ``ptr_shift`` moved by that many bytes); outputs pre-filled with
+    the canary."""
+    A, BS, K1, H = area["A"], area["BS"], area["K1"], area["H"]
+    Y = A * BS * K1
+    td = area["token_dtype"]
+    info = dev(area["info"])
+    data = dev(area["data"].reshape(-1))
+    f = ctx_fields(area, info, data, polling)
+    f.update(ctx_over or {})
+    for k, v in (ptr_shift or {}).items():
+        f[k] += v
+    ctx_bytes = synth.schedule_context(**f)
+    out = {"y": _canary((Y, H), _TOKEN_TORCH[td]),
+           "group_list": _canary((area["expert_num"], 2), torch.int64),
+           "actual_token_num": _canary((1,), torch.int64),
+           "err_count": _canary((1,), torch.int32), "ctx_status": _canary((1,), torch.int32)}
+    for k in ("session_ids", "micro_batch_ids", "token_ids", "expert_offsets"):
+        out[k] = _canary((Y,), torch.int32)
+    if td == 2:
+        out["dynamic_scale"] = _canary((Y,), torch.float32)
+    call = F.BatchingCtxCall(dev(ctx_bytes), expert_num=area["expert_num"], layer_num=area["layer_num"],
+                             max_out_shape=(A, BS, K1, H), token_dtype=td, need_schedule=need_schedule, out=out,
+                             ev_gather=ev_gather)
+    call._keep += [info, data]
+    call.ctx_bytes = ctx_bytes
+    call.need_schedule = need_schedule
+    return call
+
+
+def oracle_ctx(area, call):
+    from oracle import ffn_worker_batching_from_context
+    return ffn_worker_batching_from_context(call.ctx_bytes, area["info"], area["data"].reshape(-1),
+                                            area["expert_num"], area["layer_num"],
+                                            (area["A"], area["BS"], area["K1"], area["H"]), area["token_dtype"],
+                                            call.need_schedule)
+
+
+def check_ctx(area, call, got=None, ref=None):
+    got = got if got is not None else fetch_batching(call)
+    ref = ref if ref is not None else oracle_ctx(area, call)
+    assert int(got["ctx_status"][0]) == ref["status"]
+    check_batching(area, got, ref)
+    return ref

@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
-    for n in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
+    for n in ("ffnwb_batching_workspace_size", "ffnwb_batching", "ffnwb_batching_ctx_workspace_size",
+              "ffnwb_batching_ctx", "moe_unpermute_workspace_size",
               "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_status_string",
               "ffnwb_abi_version"):
         assert n in names
@@ -39,7 +40,8 @@ def test_descriptor_layout_and_version():
     assert L.ffnwb_batching_desc_size() == ctypes.sizeof(F.BatchingDesc)
     assert L.moe_unpermute_desc_size() == ctypes.sizeof(F.UnpermuteDesc)
     assert L.moe_permute_desc_size() == ctypes.sizeof(F.PermuteDesc)
-    assert F.ffnwb_abi_version() == 3
+    assert L.ffnwb_batching_ctx_desc_size() == ctypes.sizeof(F.BatchingCtxDesc)
+    assert F.ffnwb_abi_version() == 4
     for st in (0, 161001, 161002, 561103, 1, 2):
         assert F.ffnwb_status_string(st).startswith("FFNWB_")
 
@@ -114,6 +116,57 @@ def test_batching_launch_rejects_small_workspace_before_any_device_work():
                                   None) == F.FFNWB_ERR_WORKSPACE
     bad = _batching_desc(expert_num=0)
     assert F.lib().ffnwb_batching(ctypes.byref(bad), None, 0, None) == F.FFNWB_ERR_PARAM_INVALID
+
+
+# ----------------------------------------------------------------------------- batching from a context
+
+def _ctx_desc(**over):
+    d = F.BatchingCtxDesc()
+    vals = dict(A=2, BS=8, K1=3, H=128, expert_num=16, layer_num=1, token_dtype=0, need_schedule=1)
+    vals.update({k: v for k, v in over.items() if k in vals})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    for p in ("schedule_context", "y", "session_ids_out", "micro_batch_ids_out", "token_ids", "expert_offsets",
+              "dynamic_scale", "group_list", "actual_token_num", "ctx_status"):
+        setattr(d, p, FAKE)
+    for k, v in over.items():
+        if k not in vals:
+            setattr(d, k, v)
+    return d
+
+
+def _cws(d):
+    n = ctypes.c_size_t(0)
+    st = F.lib().ffnwb_batching_ctx_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_ctx_valid_needs_workspace_for_the_decoded_slots():
+    st, n = _cws(_ctx_desc())
+    assert st == 0 and n >= 48 * 5              # expert id + mask of each of the 48 slots
+    assert _cws(_ctx_desc(need_schedule=0))[0] == 0
+
+
+@pytest.mark.parametrize("field", ["schedule_context", "ctx_status", "y", "session_ids_out", "micro_batch_ids_out",
+                                   "token_ids", "expert_offsets", "group_list", "actual_token_num"])
+def test_ctx_required_pointers(field):
+    assert _cws(_ctx_desc(**{field: None}))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+
+
+@pytest.mark.parametrize("over", [
+    dict(need_schedule=2), dict(need_schedule=-1), dict(schedule_context=FAKE + 4), dict(A=0), dict(A=1025),
+    dict(K1=65), dict(expert_num=0), dict(token_dtype=3), dict(expert_num=16, layer_num=3),
+])
+def test_ctx_invalid_parameters(over):
+    assert _cws(_ctx_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_ctx_launch_rejects_small_workspace_before_any_device_work():
+    d = _ctx_desc()
+    st, n = _cws(d)
+    assert F.lib().ffnwb_batching_ctx(ctypes.byref(d), None, ctypes.c_size_t(n), None) == F.FFNWB_ERR_WORKSPACE
+    assert F.lib().ffnwb_batching_ctx(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_size_t(n - 1),
+                                      None) == F.FFNWB_ERR_WORKSPACE
 
 
 # ----------------------------------------------------------------------------- unpermute

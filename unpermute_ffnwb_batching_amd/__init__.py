@@ -6,6 +6,7 @@ kernels.  PyTorch provides device memory and the current HIP stream.
 The names mirror the C ABI:
 
 * ``ffnwb_batching_workspace_size`` / ``ffnwb_batching``
+* ``ffnwb_batching_ctx_workspace_size`` / ``ffnwb_batching_ctx`` (ScheduleContext input)
 * ``moe_unpermute_workspace_size`` / ``moe_unpermute``
 * ``moe_permute_workspace_size`` / ``moe_permute``
 * ``ffnwb_status_string``, ``ffnwb_abi_version``
@@ -28,7 +29,8 @@ from . import _abi
 from ._abi import (FFNWB_OK, FFNWB_ERR_PARAM_NULLPTR, FFNWB_ERR_PARAM_INVALID,  # noqa: F401
                    FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME,
                    FFNWB_DT_FP16, FFNWB_DT_BF16, FFNWB_DT_INT8, FFNWB_DT_FP32,
-                   BatchingDesc, UnpermuteDesc, PermuteDesc)
+                   FFNWB_CTX_BYTES, FFNWB_CTX_SHAPE, FFNWB_CTX_POLLING, FFNWB_CTX_POINTER,
+                   FFNWB_CTX_BUFFER, BatchingDesc, BatchingCtxDesc, UnpermuteDesc, PermuteDesc)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libffnwb.so")
 _lib = None
@@ -51,19 +53,24 @@ def lib():
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.ffnwb_batching_workspace_size.argtypes = [ctypes.POINTER(BatchingDesc), ctypes.POINTER(sz)]
         L.ffnwb_batching.argtypes = [ctypes.POINTER(BatchingDesc), vp, sz, vp]
+        L.ffnwb_batching_ctx_workspace_size.argtypes = [ctypes.POINTER(BatchingCtxDesc), ctypes.POINTER(sz)]
+        L.ffnwb_batching_ctx.argtypes = [ctypes.POINTER(BatchingCtxDesc), vp, sz, vp]
         L.moe_unpermute_workspace_size.argtypes = [ctypes.POINTER(UnpermuteDesc), ctypes.POINTER(sz)]
         L.moe_unpermute.argtypes = [ctypes.POINTER(UnpermuteDesc), vp, sz, vp]
         L.moe_permute_workspace_size.argtypes = [ctypes.POINTER(PermuteDesc), ctypes.POINTER(sz)]
         L.moe_permute.argtypes = [ctypes.POINTER(PermuteDesc), vp, sz, vp]
-        for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "moe_unpermute_workspace_size",
+        for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "ffnwb_batching_ctx_workspace_size",
+                  "ffnwb_batching_ctx", "moe_unpermute_workspace_size",
                   "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.ffnwb_status_string.argtypes = [ctypes.c_int]
         L.ffnwb_status_string.restype = ctypes.c_char_p
         L.ffnwb_batching_desc_size.restype = sz
+        L.ffnwb_batching_ctx_desc_size.restype = sz
         L.moe_unpermute_desc_size.restype = sz
         L.moe_permute_desc_size.restype = sz
         if L.ffnwb_batching_desc_size() != ctypes.sizeof(BatchingDesc) or \
+                L.ffnwb_batching_ctx_desc_size() != ctypes.sizeof(BatchingCtxDesc) or \
                 L.moe_unpermute_desc_size() != ctypes.sizeof(UnpermuteDesc) or \
                 L.moe_permute_desc_size() != ctypes.sizeof(PermuteDesc):
             raise RuntimeError("libffnwb descriptor layout does not match the Python binding")
@@ -216,6 +223,91 @@ class BatchingCall:
 def ffnwb_batching(token_data, expert_ids, *, stream=None, **kw):
     """Run FFN-worker batching once; returns the dict of output tensors."""
     return BatchingCall(token_data, expert_ids, **kw).run(stream)
+
+
+def ffnwb_batching_ctx_workspace_size(desc):
+    n = ctypes.c_size_t(0)
+    st = lib().ffnwb_batching_ctx_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != FFNWB_OK:
+        raise FfnwbError(st, "ffnwb_batching_ctx_workspace_size")
+    return n.value
+
+
+class BatchingCtxCall:
+    """A prepared ffnwb_batching_ctx call.
+
+    ``schedule_context`` is a device tensor holding the 1024 context bytes (8-byte
+    aligned); the data area it points to is device memory the caller keeps alive.
+    Outputs are allocated unless given in ``out``; ``ctx_status`` holds the context
+    check after the call has run.
+    """
+
+    def __init__(self, schedule_context, *, expert_num, layer_num, max_out_shape, token_dtype, need_schedule=0,
+                 out=None, with_err_count=True, workspace=None, ev_gather=None):
+        A, BS, K1, H = (int(v) for v in max_out_shape)
+        Y = A * BS * K1
+        dev = schedule_context.device
+        out = dict(out or {})
+        i32 = dict(dtype=torch.int32, device=dev)
+        if "y" not in out:
+            out["y"] = torch.empty((Y, H), dtype=_TOKEN_TORCH[int(token_dtype)], device=dev)
+        if "group_list" not in out:
+            out["group_list"] = torch.empty((int(expert_num), 2), dtype=torch.int64, device=dev)
+        if "actual_token_num" not in out:
+            out["actual_token_num"] = torch.empty(1, dtype=torch.int64, device=dev)
+        for k in ("session_ids", "micro_batch_ids", "token_ids", "expert_offsets"):
+            if k not in out:
+                out[k] = torch.empty(Y, **i32)
+        if int(token_dtype) == FFNWB_DT_INT8 and "dynamic_scale" not in out:
+            out["dynamic_scale"] = torch.empty(Y, dtype=torch.float32, device=dev)
+        if with_err_count and "err_count" not in out:
+            out["err_count"] = torch.empty(1, **i32)
+        if "ctx_status" not in out:
+            out["ctx_status"] = torch.empty(1, **i32)
+        self.out = out
+        self._keep = [schedule_context]
+
+        d = BatchingCtxDesc()
+        d.A, d.BS, d.K1, d.H = A, BS, K1, H
+        d.expert_num = int(expert_num)
+        d.layer_num = int(layer_num)
+        d.token_dtype = int(token_dtype)
+        d.need_schedule = int(need_schedule)
+        d.schedule_context = _ptr(schedule_context)
+        d.y = _ptr(out["y"])
+        d.session_ids_out = _ptr(out["session_ids"])
+        d.micro_batch_ids_out = _ptr(out["micro_batch_ids"])
+        d.token_ids = _ptr(out["token_ids"])
+        d.expert_offsets = _ptr(out["expert_offsets"])
+        d.dynamic_scale = _ptr(out.get("dynamic_scale"))
+        d.group_list = _ptr(out["group_list"])
+        d.actual_token_num = _ptr(out["actual_token_num"])
+        d.err_count = _ptr(out.get("err_count"))
+        d.ctx_status = _ptr(out["ctx_status"])
+        if ev_gather is not None:
+            d.ev_gather_begin = _event_handle(ev_gather[0])
+            d.ev_gather_end = _event_handle(ev_gather[1])
+        self.desc = d
+        self.ws_bytes = ffnwb_batching_ctx_workspace_size(d)
+        if workspace is None and self.ws_bytes:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+
+    def set_gather_events(self, begin, end):
+        self.desc.ev_gather_begin = _event_handle(begin)
+        self.desc.ev_gather_end = _event_handle(end)
+
+    def run(self, stream=None):
+        st = lib().ffnwb_batching_ctx(ctypes.byref(self.desc), _ptr(self.workspace), ctypes.c_size_t(self.ws_bytes),
+                                      _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "ffnwb_batching_ctx")
+        return self.out
+
+
+def ffnwb_batching_ctx(schedule_context, *, stream=None, **kw):
+    """Run FFN-worker batching from a ScheduleContext once; returns the output tensors."""
+    return BatchingCtxCall(schedule_context, **kw).run(stream)
 
 
 # ----------------------------------------------------------------------------- unpermute

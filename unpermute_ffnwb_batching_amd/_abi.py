@@ -2,7 +2,7 @@
 
 import ctypes
 
-FFNWB_ABI_VERSION = 3
+FFNWB_ABI_VERSION = 4
 
 FFNWB_OK = 0
 FFNWB_ERR_PARAM_NULLPTR = 161001
@@ -15,6 +15,12 @@ FFNWB_DT_FP16 = 0
 FFNWB_DT_BF16 = 1
 FFNWB_DT_INT8 = 2
 FFNWB_DT_FP32 = 3
+
+FFNWB_CTX_BYTES = 1024
+FFNWB_CTX_SHAPE = 1
+FFNWB_CTX_POLLING = 2
+FFNWB_CTX_POINTER = 4
+FFNWB_CTX_BUFFER = 8
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 
@@ -31,6 +37,19 @@ class BatchingDesc(ctypes.Structure):
         ("y", _vp), ("session_ids_out", _vp), ("micro_batch_ids_out", _vp),
         ("token_ids", _vp), ("expert_offsets", _vp), ("dynamic_scale", _vp),
         ("group_list", _vp), ("actual_token_num", _vp), ("err_count", _vp),
+        ("ev_gather_begin", _vp), ("ev_gather_end", _vp),
+    ]
+
+
+class BatchingCtxDesc(ctypes.Structure):
+    _fields_ = [
+        ("A", _i64), ("BS", _i64), ("K1", _i64), ("H", _i64),
+        ("expert_num", _i64), ("layer_num", _i64),
+        ("token_dtype", _i32), ("need_schedule", _i32),
+        ("schedule_context", _vp),
+        ("y", _vp), ("session_ids_out", _vp), ("micro_batch_ids_out", _vp),
+        ("token_ids", _vp), ("expert_offsets", _vp), ("dynamic_scale", _vp),
+        ("group_list", _vp), ("actual_token_num", _vp), ("err_count", _vp), ("ctx_status", _vp),
         ("ev_gather_begin", _vp), ("ev_gather_end", _vp),
     ]
 

@@ -34,6 +34,8 @@ int ffnwb_abi_version(void) { return FFNWB_ABI_VERSION; }
 
 size_t ffnwb_batching_desc_size(void) { return sizeof(ffnwb_batching_desc); }
 
+size_t ffnwb_batching_ctx_desc_size(void) { return sizeof(ffnwb_batching_ctx_desc); }
+
 size_t moe_unpermute_desc_size(void) { return sizeof(moe_unpermute_desc); }
 
 size_t moe_permute_desc_size(void) { return sizeof(moe_permute_desc); }
@@ -65,6 +67,23 @@ int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_byte
   if (st != FFNWB_OK) return st;
   if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
   return launch_batching(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int ffnwb_batching_ctx_workspace_size(const ffnwb_batching_ctx_desc* d, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  BatchingCtxPlan p;
+  const int st = plan_batching_ctx(d, &p);
+  if (st != FFNWB_OK) return st;
+  *ws_bytes = p.ws_bytes;
+  return FFNWB_OK;
+}
+
+int ffnwb_batching_ctx(const ffnwb_batching_ctx_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  BatchingCtxPlan p;
+  const int st = plan_batching_ctx(d, &p);
+  if (st != FFNWB_OK) return st;
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  return launch_batching_ctx(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 
 int moe_unpermute_workspace_size(const moe_unpermute_desc* d, size_t* ws_bytes) {

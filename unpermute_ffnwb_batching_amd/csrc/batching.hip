@@ -39,7 +39,24 @@ struct BatchArgs {
   int32_t* token_ids;
   int32_t* offsets;
   float* dyn_scale;           // nullptr unless INT8
+  const uint64_t* chunk_src;  // context mode: address of each chunk's first row, else nullptr
 };
+
+// Source row of slot s: token_data + s * stride, or in context mode entry s % chunk of
+// chunk s / chunk, whose rows start at chunk_src[chunk] (the branch is uniform).
+__device__ __forceinline__ const uint8_t* slot_row(const BatchArgs& a, int64_t s) {
+  if (a.chunk_src == nullptr) return a.token_data + s * a.stride;
+  const uint32_t chunk = static_cast<uint32_t>(a.chunk);
+  const uint32_t c = static_cast<uint32_t>(s) / chunk;
+  const uint32_t j = static_cast<uint32_t>(s) - c * chunk;
+  return reinterpret_cast<const uint8_t*>(a.chunk_src[c]) + static_cast<int64_t>(j) * a.stride;
+}
+
+// INT8 dynamic scale of slot s; in context mode packed after the row's H bytes.
+__device__ __forceinline__ const uint8_t* slot_scale(const BatchArgs& a, int64_t s) {
+  if (a.chunk_src == nullptr) return a.scale_base + s * a.scale_stride;
+  return slot_row(a, s) + a.row_bytes;
+}
 
 // Slot key: layer * experts_per_layer + expert id; masked slots do not take part, and
 // unmasked slots with an out-of-range expert or layer id are dropped and counted.
@@ -126,7 +143,7 @@ __device__ __forceinline__ void write_row_ids(const BatchArgs& a, int64_t s, uin
   a.offsets[pos] = static_cast<int32_t>(pos - first);
   a.session_out[pos] = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
   a.mb_out[pos] = a.micro_batch_ids ? a.micro_batch_ids[c] : 0;
-  if (a.dyn_scale != nullptr) a.dyn_scale[pos] = load_scale(a.scale_base + s * a.scale_stride);
+  if (a.dyn_scale != nullptr) a.dyn_scale[pos] = load_scale(slot_scale(a, s));
 }
 
 // One wavefront per source slot (4 slots per workgroup).  The slot's output row is
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(256) void batching_gather_kernel(BatchArgs a, Place
   const uint32_t p = uniform(pl.packed[s]);
   if (p == kNoRank) return;
   const uint32_t lane = lane_id();
-  const uint8_t* src = a.token_data + s * a.stride;
+  const uint8_t* src = slot_row(a, s);
   const int64_t n16 = a.row_bytes >> 4;
   RowPiece<VEC> first;
   if (VEC != 1) first.load(src, n16, 0, lane);
@@ -266,8 +283,8 @@ __global__ __launch_bounds__(256) void batching_copy_kernel(BatchArgs a, const u
   const uint32_t pos = uniform(pos_of[s]);
   if (pos == kNoRank) return;
   const uint32_t lane = lane_id();
-  copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
-  if (a.dyn_scale != nullptr && lane == 0) a.dyn_scale[pos] = load_scale(a.scale_base + s * a.scale_stride);
+  copy_row<VEC>(slot_row(a, s), a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+  if (a.dyn_scale != nullptr && lane == 0) a.dyn_scale[pos] = load_scale(slot_scale(a, s));
 }
 
 // All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
       const uint32_t key = ks.key(s, v, e);
       write_row_ids(a, s, pos, start[key]);
     }
-    copy_row<VEC>(a.token_data + s * a.stride, a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+    copy_row<VEC>(slot_row(a, s), a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
   }
 }
 
@@ -405,9 +422,10 @@ SortPlan make_sort_plan(int64_t n, uint64_t nkeys) {
 }
 
 
-int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
+int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p, bool from_context) {
   if (d == nullptr || p == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
-  if (d->token_data == nullptr || d->expert_ids == nullptr || d->y == nullptr || d->session_ids_out == nullptr ||
+  if (!from_context && (d->token_data == nullptr || d->expert_ids == nullptr)) return FFNWB_ERR_PARAM_NULLPTR;
+  if (d->y == nullptr || d->session_ids_out == nullptr ||
       d->micro_batch_ids_out == nullptr || d->token_ids == nullptr || d->expert_offsets == nullptr ||
       d->group_list == nullptr || d->actual_token_num == nullptr)
     return FFNWB_ERR_PARAM_NULLPTR;
@@ -440,7 +458,7 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
   p->stride = stride;
   if (int8) {
     if (packed_scale) {
-      p->scale_base = static_cast<const uint8_t*>(d->token_data) + row;
+      p->scale_base = from_context ? nullptr : static_cast<const uint8_t*>(d->token_data) + row;
       p->scale_stride = stride;
     } else {
       p->scale_base = reinterpret_cast<const uint8_t*>(d->token_scale);
@@ -449,7 +467,8 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p) {
   }
   const int nb = static_cast<int>(d->expert_num);
   p->pass = make_pass(Y, nb, bits_for(static_cast<uint64_t>(nb - 1)), 0);
-  p->vec = vec_class(reinterpret_cast<uintptr_t>(d->token_data), reinterpret_cast<uintptr_t>(d->y), stride, row, row);
+  const uintptr_t base = from_context ? 0 : reinterpret_cast<uintptr_t>(d->token_data);
+  p->vec = vec_class(base, reinterpret_cast<uintptr_t>(d->y), stride, row, row);
   p->small = (p->pass.nt == 1) && p->pass.R == 4 && nb <= 4096 && Y * row <= (int64_t{1} << 22);
   // the slot key reads three inputs, so the one-launch order pays off only for moderate
   // slot counts (measured crossover with the rank / scan / gather path: ~8K slots)
@@ -479,7 +498,8 @@ static hipError_t launch_vec(int vec, F&& f) {
   return hipGetLastError();
 }
 
-int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s) {
+int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s,
+                    const uint64_t* chunk_src) {
   BatchArgs a{};
   a.Y = p.Y;
   a.chunk = d->BS * d->K1;
@@ -502,6 +522,7 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   a.token_ids = d->token_ids;
   a.offsets = d->expert_offsets;
   a.dyn_scale = (d->token_dtype == FFNWB_DT_INT8) ? d->dynamic_scale : nullptr;
+  a.chunk_src = chunk_src;
   const int nb = p.pass.nb;
   hipError_t err = hipSuccess;
 

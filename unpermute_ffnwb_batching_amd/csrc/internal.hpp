@@ -71,8 +71,23 @@ struct BatchingPlan {
   size_t ws_bytes = 0;
 };
 
-int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p);
-int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s);
+// from_context: the rows and per-slot inputs come from the ScheduleContext decode, so
+// their pointers are not checked here and the row base counts as 16-byte aligned (the
+// decode verifies that on the device before any row is read).
+int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p, bool from_context = false);
+// chunk_src (context mode): device array of the address of each chunk's first row; the
+// rows of a chunk follow each other `stride` bytes apart.  NULL: rows from d->token_data.
+int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* ws, hipStream_t s,
+                    const uint64_t* chunk_src = nullptr);
+
+struct BatchingCtxPlan {
+  BatchingPlan flat;    // the batching of the decoded slots
+  size_t flat_ws = 0;   // its part of the workspace (first)
+  size_t ws_bytes = 0;  // plus the decoded per-slot and per-chunk arrays
+};
+
+int plan_batching_ctx(const ffnwb_batching_ctx_desc* d, BatchingCtxPlan* p);
+int launch_batching_ctx(const ffnwb_batching_ctx_desc* d, const BatchingCtxPlan& p, void* ws, hipStream_t s);
 
 struct UnpermutePlan {
   int64_t T = 0, H = 0, N = 0, E = 0, rows = 0, K = 0, C = 0;
