@@ -36,3 +36,4 @@ from .batching import ffn_worker_batching  # noqa: F401
 from .unpermute import moe_token_unpermute_with_routing_map  # noqa: F401
 from .permute import moe_token_permute_with_routing_map  # noqa: F401
 from .schedule import ffn_worker_batching_from_context, decode_schedule_context  # noqa: F401
+from .update_expert import moe_update_expert  # noqa: F401

@@ -395,3 +395,56 @@ def schedule_area(seed, A, M, BS, K1, H, expert_num, layer_num, token_dtype, n_n
     return dict(info=info, data=data, flags=flags, layers=layers, expert_ids=ids, row=row,
                 A=A, M=M, BS=BS, K1=K1, H=H, expert_num=expert_num, layer_num=layer_num,
                 token_dtype=token_dtype)
+
+
+# ----------------------------------------------------------------------------- expert update
+
+def eplb_table(rng, E, world_size, place_per_rank, F):
+    """An expert-placement table: W*P physical instances, each hosting one logical
+    expert; every expert has at least one instance, the W*P - E spare instances go to
+    random experts as extra replicas (at most F - 1 per expert).  Row e = [count,
+    distinct instance ids, then -1 padding]."""
+    n_inst = world_size * place_per_rank
+    assert E <= n_inst <= E * (F - 1)
+    inst = rng.permutation(n_inst).astype(np.int32)
+    rows = [[int(inst[e])] for e in range(E)]
+    for i in inst[E:]:
+        while True:
+            e = int(rng.integers(0, E))
+            if len(rows[e]) < F - 1:
+                rows[e].append(int(i))
+                break
+    table = np.full((E, F), -1, dtype=np.int32)
+    for e, r in enumerate(rows):
+        table[e, 0] = len(r)
+        table[e, 1:1 + len(r)] = r
+    return table
+
+
+def update_expert_case(seed, BS, K, E, world_size, place_per_rank, F=None, local_rank_id=0, balance_mode=0,
+                       id_dtype=np.int32, scale_dtype=None, n_active=None, keep_frac=0.8, n_bad_ids=0):
+    """MoeUpdateExpert input: each token's K distinct logical experts (uniform), the
+    placement table, and optionally descending softmax scales of the token's experts
+    with a per-slot threshold that prunes about 1 - keep_frac of the slots, and an
+    active mask whose first n_active tokens are true."""
+    rng = np.random.default_rng(seed)
+    F = F if F is not None else world_size + 1
+    table = eplb_table(rng, E, world_size, place_per_rank, F)
+    ids = np.stack([rng.choice(E, size=K, replace=False) for _ in range(BS)]).astype(id_dtype)
+    if n_bad_ids:
+        flat = ids.reshape(-1)
+        bad = rng.choice(flat.size, size=n_bad_ids, replace=False)
+        flat[bad] = rng.choice(np.array([-1, E, E + 7]), size=n_bad_ids).astype(id_dtype)
+    scales = thr = active = None
+    if scale_dtype is not None:
+        logits = rng.standard_normal((BS, K))
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p = -np.sort(-(p / p.sum(axis=1, keepdims=True)), axis=1)
+        scales = _probs_storage(p, scale_dtype)
+        thr = np.quantile(p, 1.0 - keep_frac, axis=0).astype(np.float32)
+        if n_active is not None:
+            active = np.zeros(BS, dtype=bool)
+            active[:n_active] = True
+    return dict(expert_ids=ids, eplb_table=table, expert_scales=scales, scale_dtype=scale_dtype,
+                pruning_threshold=thr, active_mask=active, local_rank_id=local_rank_id, world_size=world_size,
+                balance_mode=balance_mode, BS=BS, K=K, E=E, F=F)
