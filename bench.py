@@ -229,6 +229,43 @@ def measure_ctx(args, stream):
     return res
 
 
+def measure_update_expert(args, stream):
+    """MoeUpdateExpert at its largest token count: BS=512 tokens x topK=8 over 256
+    logical experts placed as 320 instances on 64 ranks (F=9), BF16 scales with a
+    per-slot threshold, 400 active tokens, balance by rank.  One launch of 4096 slots:
+    its time is latency (three dependent load rounds), not bandwidth."""
+    import torch
+    import synth
+    from _gpu import prepare_update_expert, check_update_expert
+    c = synth.update_expert_case(15, 512, 8, 256, 64, 5, F=9, local_rank_id=37, scale_dtype=synth.BF16,
+                                 n_active=400)
+    call = prepare_update_expert(c)
+    for _ in range(3):
+        call.run(stream)
+    torch.cuda.synchronize()
+    K = max(args.steps, 5) * 10
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(K):
+        call.run(stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    us = s0.elapsed_time(s1) / K * 1e3
+    n = 512 * 8
+    res = {"shape": "BS=512 topK=8, 256 experts on 64 ranks x 5 instances, F=9, bf16 scales, by rank",
+           "us_per_call": round(us, 2), "slots_per_s": round(n / us * 1e6, 1)}
+    if not args.no_cpu_baseline:
+        t1 = time.perf_counter()
+        try:
+            check_update_expert(c, call)
+            res["parity"] = True
+        except AssertionError as ex:
+            res["parity"] = False
+            print(f"# parity FAILED for the expert update: {ex}", file=sys.stderr, flush=True)
+        res["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+    return res
+
+
 def measure_permute(args, stream):
     """The forward permute (a widening of the path) at the non-padded workload's shape:
     flushed-cache medians, the row-copy kernel's steady-state time from fence-free HIP
@@ -475,6 +512,8 @@ def main():
         next_rows["moe_permute_nonpadded"] = measure_permute(args, stream)
     if not args.only or "context" in args.only.split(","):
         next_rows["batching_from_context"] = measure_ctx(args, stream)
+    if not args.only or "update_expert" in args.only.split(","):
+        next_rows["moe_update_expert"] = measure_update_expert(args, stream)
     if "unpermute_padded" in cases:
         next_rows["unpermute_padded_skip_zero_weight"] = measure_skip(args, stream, cases["unpermute_padded"])
     next_rows = next_rows or None

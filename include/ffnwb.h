@@ -20,6 +20,9 @@
  *                      the attention->FFN data area ("Function description" step 1,
  *                      the scheduleContext / needSchedule rows of the parameter table,
  *                      the usage example's packed struct definitions).
+ *   moe_update_expert -- logical -> physical expert instances through a placement
+ *                      table, with threshold pruning (MoeUpdateExpert README:
+ *                      "Function description", the parameter table, "Constraints").
  *   moe_permute     -- the forward permute the same article names in "Operator
  *                      positioning"; its outputs are the arrangement the
  *                      unpermute's formulas invert (see its section below).
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FFNWB_ABI_VERSION 4
+#define FFNWB_ABI_VERSION 5
 
 /* Status codes.  The first three take the aclnn values both pages list. */
 #define FFNWB_OK                 0
@@ -67,6 +70,8 @@ extern "C" {
 #define FFNWB_DT_BF16 1
 #define FFNWB_DT_INT8 2 /* batching: INT8 data with an FP32 dynamic scale per row; permute: 1-byte elements */
 #define FFNWB_DT_FP32 3 /* unpermute and permute */
+#define FFNWB_DT_INT32 4 /* moe_update_expert ids */
+#define FFNWB_DT_INT64 5 /* moe_update_expert ids */
 
 /* ------------------------------------------------------------------------------------------
  * FFN-worker batching (aclnnFfnWorkerBatching API page).
@@ -335,6 +340,55 @@ int moe_permute_workspace_size(const moe_permute_desc* d, size_t* ws_bytes);
 /* Validates again, then enqueues the permute on `stream`. */
 int moe_permute(const moe_permute_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * MoeUpdateExpert (its README page: "Function description", the parameter table,
+ * "Constraints").
+ *
+ * For every token t < BS and slot k < K with logical expert e = expert_ids[t*K + k]:
+ *   balanced_expert_ids[t*K + k] = eplb_table[e*F + 1 + r],
+ *     r = local_rank_id mod count (balance_mode 0, by rank) or t mod count (balance_mode
+ *     1, by token), count = eplb_table[e*F]: each table row is [count, the instance ids
+ *     of the expert's replicas].
+ *   With scales: balanced_active_mask[t*K + k] = 1 when the token is active (active_mask
+ *   NULL or active_mask[t] != 0) and NOT expert_scales[t*K + k] < pruning_threshold[k]
+ *   (FP32 comparison: equal is kept, NaN is kept); 0 otherwise.
+ * An expert id outside [0, moe_expert_num) or a count outside [1, F-1] gives -1, mask 0,
+ * and is counted in *err_count.  Table rows are only read at columns 0 .. count.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct moe_update_expert_desc {
+  int64_t bs;               /* BS in (0, 512] */
+  int64_t k;                /* K in (0, 16], K <= moe_expert_num */
+  int64_t moe_expert_num;   /* E in (0, 1024] */
+  int64_t table_cols;       /* F in [2, world_size + 1] */
+  int64_t local_rank_id;    /* balance_mode 0: in [0, world_size) */
+  int64_t world_size;       /* balance_mode 0: in [2, 768]; balance_mode 1: in [1, 768] */
+  int32_t balance_mode;     /* 0 = distribute by rank, 1 = by token */
+  int32_t id_dtype;         /* FFNWB_DT_INT32 or FFNWB_DT_INT64, for ids in and out */
+  int32_t scale_dtype;      /* FFNWB_DT_FP16, _BF16 or _FP32; ignored without scales */
+  int32_t reserved0;        /* must be 0 */
+
+  /* Inputs (dense, row-major). */
+  const void* expert_ids;          /* [BS, K] of id_dtype */
+  const int32_t* eplb_table;       /* [E, F] */
+  const void* expert_scales;       /* [BS, K] of scale_dtype, or NULL */
+  const float* pruning_threshold;  /* [K], or NULL; NULL exactly when expert_scales is */
+  const uint8_t* active_mask;      /* [BS] bool, or NULL (= all active); only with scales */
+
+  /* Outputs. */
+  void* balanced_expert_ids;       /* [BS, K] of id_dtype, required */
+  uint8_t* balanced_active_mask;   /* [BS, K] bool; required with scales, ignored without */
+  int32_t* err_count;              /* [1] or NULL */
+} moe_update_expert_desc;
+
+/* Validates *d and returns the workspace size (0) (host only).  Errors:
+   FFNWB_ERR_PARAM_NULLPTR (d, ws_bytes or a required pointer NULL),
+   FFNWB_ERR_PARAM_INVALID (a range above violated, dtype codes, scales given without a
+   threshold or the other way round, active_mask without scales, reserved0 != 0). */
+int moe_update_expert_workspace_size(const moe_update_expert_desc* d, size_t* ws_bytes);
+
+/* Validates again, then enqueues the update on `stream` (one launch). */
+int moe_update_expert(const moe_update_expert_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* ffnwb_status_string(int status);
 
@@ -346,6 +400,7 @@ size_t ffnwb_batching_desc_size(void);
 size_t ffnwb_batching_ctx_desc_size(void);
 size_t moe_unpermute_desc_size(void);
 size_t moe_permute_desc_size(void);
+size_t moe_update_expert_desc_size(void);
 
 #ifdef __cplusplus
 }

@@ -289,3 +289,45 @@ def check_ctx(area, call, got=None, ref=None):
     assert int(got["ctx_status"][0]) == ref["status"]
     check_batching(area, got, ref)
     return ref
+
+
+# ----------------------------------------------------------------------------- expert update
+
+def prepare_update_expert(case, rank=None, mode=None):
+    ids = dev(case["expert_ids"])
+    BS, K = case["expert_ids"].shape
+    out = {"balanced_expert_ids": _canary((BS, K), ids.dtype), "err_count": _canary((1,), torch.int32)}
+    scales = thr = active = None
+    if case["expert_scales"] is not None:
+        scales = to_torch_elems(case["expert_scales"], case["scale_dtype"])
+        thr = dev(case["pruning_threshold"])
+        out["balanced_active_mask"] = _canary((BS, K), torch.uint8).view(torch.bool)
+        if case["active_mask"] is not None:
+            active = dev(case["active_mask"])
+    return F.UpdateExpertCall(ids, dev(case["eplb_table"]),
+                              local_rank_id=case["local_rank_id"] if rank is None else rank,
+                              world_size=case["world_size"], balance_mode=case["balance_mode"] if mode is None else mode,
+                              expert_scales=scales, pruning_threshold=thr, active_mask=active, out=out)
+
+
+def oracle_update_expert(case, rank=None, mode=None):
+    from oracle import moe_update_expert
+    from oracle import numerics as nm
+    s = None if case["expert_scales"] is None else nm.to_f32(case["expert_scales"], case["scale_dtype"])
+    return moe_update_expert(case["expert_ids"], case["eplb_table"],
+                             case["local_rank_id"] if rank is None else rank, case["world_size"],
+                             case["balance_mode"] if mode is None else mode, s, case["pruning_threshold"],
+                             case["active_mask"])
+
+
+def check_update_expert(case, call, rank=None, mode=None):
+    ref = oracle_update_expert(case, rank, mode)
+    o = call.out
+    got_ids = o["balanced_expert_ids"].cpu().numpy()
+    assert got_ids.dtype == ref["balanced_expert_ids"].dtype
+    assert np.array_equal(got_ids, ref["balanced_expert_ids"])
+    assert int(o["err_count"][0]) == ref["err_count"]
+    if ref["balanced_active_mask"] is not None:
+        m = o["balanced_active_mask"].view(torch.uint8).cpu().numpy()
+        assert np.array_equal(m, ref["balanced_active_mask"].astype(np.uint8))
+    return ref

@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
     for n in ("ffnwb_batching_workspace_size", "ffnwb_batching", "ffnwb_batching_ctx_workspace_size",
-              "ffnwb_batching_ctx", "moe_unpermute_workspace_size",
+              "ffnwb_batching_ctx", "moe_update_expert_workspace_size", "moe_update_expert",
+              "moe_unpermute_workspace_size",
               "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_status_string",
               "ffnwb_abi_version"):
         assert n in names
@@ -41,7 +42,8 @@ def test_descriptor_layout_and_version():
     assert L.moe_unpermute_desc_size() == ctypes.sizeof(F.UnpermuteDesc)
     assert L.moe_permute_desc_size() == ctypes.sizeof(F.PermuteDesc)
     assert L.ffnwb_batching_ctx_desc_size() == ctypes.sizeof(F.BatchingCtxDesc)
-    assert F.ffnwb_abi_version() == 4
+    assert L.moe_update_expert_desc_size() == ctypes.sizeof(F.UpdateExpertDesc)
+    assert F.ffnwb_abi_version() == 5
     for st in (0, 161001, 161002, 561103, 1, 2):
         assert F.ffnwb_status_string(st).startswith("FFNWB_")
 
@@ -302,3 +304,59 @@ def test_permute_workspace():
     assert st == 0 and n >= 4 * 16384 * 8            # source token of every row
     st, n = _pws(_permute_desc(padded_mode=1, num_tokens=8192, num_experts=64, num_out_rows=64 * 512, capacity=512))
     assert st == 0 and n >= 4 * 32 * 64               # tile histogram only
+
+
+# ----------------------------------------------------------------------------- expert update
+
+def _ue_desc(scales=True, **over):
+    d = F.UpdateExpertDesc()
+    vals = dict(bs=512, k=8, moe_expert_num=256, table_cols=9, local_rank_id=3, world_size=64, balance_mode=0,
+                id_dtype=4, scale_dtype=1, reserved0=0)
+    vals.update({k: v for k, v in over.items() if k in vals})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    for p in ("expert_ids", "eplb_table", "balanced_expert_ids"):
+        setattr(d, p, FAKE)
+    if scales:
+        for p in ("expert_scales", "pruning_threshold", "balanced_active_mask"):
+            setattr(d, p, FAKE)
+    for k, v in over.items():
+        if k not in vals:
+            setattr(d, k, v)
+    return d
+
+
+def _uews(d):
+    n = ctypes.c_size_t(7)
+    st = F.lib().moe_update_expert_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_update_expert_valid_needs_no_workspace():
+    assert _uews(_ue_desc()) == (0, 0)
+    assert _uews(_ue_desc(scales=False)) == (0, 0)
+    assert _uews(_ue_desc(active_mask=FAKE))[0] == 0
+    for over in (dict(bs=1, k=1, moe_expert_num=1), dict(k=16), dict(moe_expert_num=1024), dict(world_size=768),
+                 dict(table_cols=65), dict(balance_mode=1, world_size=1, table_cols=2, local_rank_id=99),
+                 dict(id_dtype=5), dict(scale_dtype=0), dict(scale_dtype=3), dict(local_rank_id=63)):
+        assert _uews(_ue_desc(**over))[0] == 0, over
+
+
+@pytest.mark.parametrize("field", ["expert_ids", "eplb_table", "balanced_expert_ids", "balanced_active_mask"])
+def test_update_expert_required_pointers(field):
+    assert _uews(_ue_desc(**{field: None}))[0] == F.FFNWB_ERR_PARAM_NULLPTR
+
+
+@pytest.mark.parametrize("over", [
+    dict(bs=0), dict(bs=513), dict(k=0), dict(k=17), dict(moe_expert_num=0), dict(moe_expert_num=1025),
+    dict(k=8, moe_expert_num=7), dict(world_size=1), dict(world_size=769), dict(local_rank_id=-1),
+    dict(local_rank_id=64), dict(table_cols=1), dict(table_cols=66), dict(balance_mode=2), dict(id_dtype=3),
+    dict(id_dtype=0), dict(scale_dtype=4), dict(reserved0=1), dict(pruning_threshold=None),
+    dict(expert_scales=None),
+])
+def test_update_expert_invalid_parameters(over):
+    assert _uews(_ue_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_update_expert_active_mask_needs_scales():
+    assert _uews(_ue_desc(scales=False, active_mask=FAKE))[0] == F.FFNWB_ERR_PARAM_INVALID

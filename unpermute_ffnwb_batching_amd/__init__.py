@@ -9,6 +9,7 @@ The names mirror the C ABI:
 * ``ffnwb_batching_ctx_workspace_size`` / ``ffnwb_batching_ctx`` (ScheduleContext input)
 * ``moe_unpermute_workspace_size`` / ``moe_unpermute``
 * ``moe_permute_workspace_size`` / ``moe_permute``
+* ``moe_update_expert_workspace_size`` / ``moe_update_expert``
 * ``ffnwb_status_string``, ``ffnwb_abi_version``
 
 ``ffnwb_batching``, ``moe_unpermute`` and ``moe_permute`` take torch tensors, allocate any
@@ -30,7 +31,8 @@ from ._abi import (FFNWB_OK, FFNWB_ERR_PARAM_NULLPTR, FFNWB_ERR_PARAM_INVALID,  
                    FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME,
                    FFNWB_DT_FP16, FFNWB_DT_BF16, FFNWB_DT_INT8, FFNWB_DT_FP32,
                    FFNWB_CTX_BYTES, FFNWB_CTX_SHAPE, FFNWB_CTX_POLLING, FFNWB_CTX_POINTER,
-                   FFNWB_CTX_BUFFER, BatchingDesc, BatchingCtxDesc, UnpermuteDesc, PermuteDesc)
+                   FFNWB_CTX_BUFFER, FFNWB_DT_INT32, FFNWB_DT_INT64, BatchingDesc, BatchingCtxDesc,
+                   UnpermuteDesc, PermuteDesc, UpdateExpertDesc)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libffnwb.so")
 _lib = None
@@ -59,9 +61,12 @@ def lib():
         L.moe_unpermute.argtypes = [ctypes.POINTER(UnpermuteDesc), vp, sz, vp]
         L.moe_permute_workspace_size.argtypes = [ctypes.POINTER(PermuteDesc), ctypes.POINTER(sz)]
         L.moe_permute.argtypes = [ctypes.POINTER(PermuteDesc), vp, sz, vp]
+        L.moe_update_expert_workspace_size.argtypes = [ctypes.POINTER(UpdateExpertDesc), ctypes.POINTER(sz)]
+        L.moe_update_expert.argtypes = [ctypes.POINTER(UpdateExpertDesc), vp, sz, vp]
         for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "ffnwb_batching_ctx_workspace_size",
                   "ffnwb_batching_ctx", "moe_unpermute_workspace_size",
-                  "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "ffnwb_abi_version"):
+                  "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "moe_update_expert_workspace_size",
+                  "moe_update_expert", "ffnwb_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.ffnwb_status_string.argtypes = [ctypes.c_int]
         L.ffnwb_status_string.restype = ctypes.c_char_p
@@ -69,10 +74,12 @@ def lib():
         L.ffnwb_batching_ctx_desc_size.restype = sz
         L.moe_unpermute_desc_size.restype = sz
         L.moe_permute_desc_size.restype = sz
+        L.moe_update_expert_desc_size.restype = sz
         if L.ffnwb_batching_desc_size() != ctypes.sizeof(BatchingDesc) or \
                 L.ffnwb_batching_ctx_desc_size() != ctypes.sizeof(BatchingCtxDesc) or \
                 L.moe_unpermute_desc_size() != ctypes.sizeof(UnpermuteDesc) or \
-                L.moe_permute_desc_size() != ctypes.sizeof(PermuteDesc):
+                L.moe_permute_desc_size() != ctypes.sizeof(PermuteDesc) or \
+                L.moe_update_expert_desc_size() != ctypes.sizeof(UpdateExpertDesc):
             raise RuntimeError("libffnwb descriptor layout does not match the Python binding")
         if L.ffnwb_abi_version() != _abi.FFNWB_ABI_VERSION:
             raise RuntimeError("libffnwb ABI version mismatch")
@@ -471,3 +478,64 @@ class PermuteCall:
 def moe_permute(tokens, routing_map, *, stream=None, **kw):
     """Run the forward permute once; returns dict(permuted_tokens, sorted_indices)."""
     return PermuteCall(tokens, routing_map, **kw).run(stream)
+
+
+# ----------------------------------------------------------------------------- expert update
+
+_ID_CODE = {torch.int32: FFNWB_DT_INT32, torch.int64: FFNWB_DT_INT64}
+
+
+def moe_update_expert_workspace_size(desc):
+    n = ctypes.c_size_t(0)
+    st = lib().moe_update_expert_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != FFNWB_OK:
+        raise FfnwbError(st, "moe_update_expert_workspace_size")
+    return n.value
+
+
+class UpdateExpertCall:
+    """A prepared moe_update_expert call.  ``expert_ids`` [BS, K] int32 / int64,
+    ``eplb_table`` [E, F] int32, optional ``expert_scales`` [BS, K] (float16, bfloat16
+    or float32) with ``pruning_threshold`` [K] float32, and optional ``active_mask`` [BS]
+    bool, all dense device tensors."""
+
+    def __init__(self, expert_ids, eplb_table, *, local_rank_id, world_size, balance_mode=0, expert_scales=None,
+                 pruning_threshold=None, active_mask=None, out=None, with_err_count=True):
+        BS, K = expert_ids.shape
+        E, Fc = eplb_table.shape
+        dev = expert_ids.device
+        out = dict(out or {})
+        if "balanced_expert_ids" not in out:
+            out["balanced_expert_ids"] = torch.empty((BS, K), dtype=expert_ids.dtype, device=dev)
+        if expert_scales is not None and "balanced_active_mask" not in out:
+            out["balanced_active_mask"] = torch.empty((BS, K), dtype=torch.bool, device=dev)
+        if with_err_count and "err_count" not in out:
+            out["err_count"] = torch.empty(1, dtype=torch.int32, device=dev)
+        self.out = out
+        self._keep = [expert_ids, eplb_table, expert_scales, pruning_threshold, active_mask]
+        d = UpdateExpertDesc()
+        d.bs, d.k, d.moe_expert_num, d.table_cols = BS, K, E, Fc
+        d.local_rank_id, d.world_size, d.balance_mode = int(local_rank_id), int(world_size), int(balance_mode)
+        d.id_dtype = _ID_CODE.get(expert_ids.dtype, -1)
+        d.scale_dtype = _FLOAT_CODE.get(expert_scales.dtype, -1) if expert_scales is not None else 0
+        d.expert_ids = _ptr(expert_ids)
+        d.eplb_table = _ptr(eplb_table)
+        d.expert_scales = _ptr(expert_scales)
+        d.pruning_threshold = _ptr(pruning_threshold)
+        d.active_mask = _ptr(active_mask)
+        d.balanced_expert_ids = _ptr(out["balanced_expert_ids"])
+        d.balanced_active_mask = _ptr(out.get("balanced_active_mask"))
+        d.err_count = _ptr(out.get("err_count"))
+        self.desc = d
+        moe_update_expert_workspace_size(d)   # validates
+
+    def run(self, stream=None):
+        st = lib().moe_update_expert(ctypes.byref(self.desc), None, ctypes.c_size_t(0), _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "moe_update_expert")
+        return self.out
+
+
+def moe_update_expert(expert_ids, eplb_table, *, stream=None, **kw):
+    """Run MoeUpdateExpert once; returns the dict of output tensors."""
+    return UpdateExpertCall(expert_ids, eplb_table, **kw).run(stream)

@@ -2,7 +2,7 @@
 
 import ctypes
 
-FFNWB_ABI_VERSION = 4
+FFNWB_ABI_VERSION = 5
 
 FFNWB_OK = 0
 FFNWB_ERR_PARAM_NULLPTR = 161001
@@ -15,6 +15,8 @@ FFNWB_DT_FP16 = 0
 FFNWB_DT_BF16 = 1
 FFNWB_DT_INT8 = 2
 FFNWB_DT_FP32 = 3
+FFNWB_DT_INT32 = 4
+FFNWB_DT_INT64 = 5
 
 FFNWB_CTX_BYTES = 1024
 FFNWB_CTX_SHAPE = 1
@@ -75,4 +77,15 @@ class PermuteDesc(ctypes.Structure):
         ("tokens", _vp), ("routing_map", _vp),
         ("permuted_tokens", _vp), ("sorted_indices", _vp),
         ("ev_copy_begin", _vp), ("ev_copy_end", _vp),
+    ]
+
+
+class UpdateExpertDesc(ctypes.Structure):
+    _fields_ = [
+        ("bs", _i64), ("k", _i64), ("moe_expert_num", _i64), ("table_cols", _i64),
+        ("local_rank_id", _i64), ("world_size", _i64),
+        ("balance_mode", _i32), ("id_dtype", _i32), ("scale_dtype", _i32), ("reserved0", _i32),
+        ("expert_ids", _vp), ("eplb_table", _vp), ("expert_scales", _vp), ("pruning_threshold", _vp),
+        ("active_mask", _vp),
+        ("balanced_expert_ids", _vp), ("balanced_active_mask", _vp), ("err_count", _vp),
     ]

@@ -40,6 +40,8 @@ size_t moe_unpermute_desc_size(void) { return sizeof(moe_unpermute_desc); }
 
 size_t moe_permute_desc_size(void) { return sizeof(moe_permute_desc); }
 
+size_t moe_update_expert_desc_size(void) { return sizeof(moe_update_expert_desc); }
+
 const char* ffnwb_status_string(int status) {
   switch (status) {
     case FFNWB_OK: return "FFNWB_OK";
@@ -118,6 +120,22 @@ int moe_permute(const moe_permute_desc* d, void* workspace, size_t ws_bytes, voi
   if (st != FFNWB_OK) return st;
   if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
   return launch_permute(d, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_update_expert_workspace_size(const moe_update_expert_desc* d, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return FFNWB_ERR_PARAM_NULLPTR;
+  const int st = plan_update_expert(d);
+  if (st != FFNWB_OK) return st;
+  *ws_bytes = 0;
+  return FFNWB_OK;
+}
+
+int moe_update_expert(const moe_update_expert_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  const int st = plan_update_expert(d);
+  if (st != FFNWB_OK) return st;
+  return launch_update_expert(d, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -115,6 +115,9 @@ struct PermutePlan {
 int plan_permute(const moe_permute_desc* d, PermutePlan* p);
 int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hipStream_t s);
 
+int plan_update_expert(const moe_update_expert_desc* d);
+int launch_update_expert(const moe_update_expert_desc* d, hipStream_t s);
+
 // Widest row-copy access (16, 4 or 1 bytes) that two base addresses, two strides and the
 // row size all allow.
 inline int vec_class(uintptr_t a, uintptr_t b, int64_t s1, int64_t s2, int64_t bytes) {
