@@ -30,6 +30,8 @@ RANDOM = [
     (2, 100, 64, 16, 5000, 1, synth.FP16, 999, 30, False, 0, False),   # K+1 = 64, 5000 keys
     (1024, 2, 1, 8, 16, 1, synth.FP16, 0, 0, True, 0, False),          # A = 1024 chunks
     (64, 512, 9, 16, 256, 2, synth.FP16, 1000, 10, True, 0, False),    # Y = 294912: multi-launch sort
+    (16, 64, 8, 32, 2048, 4, synth.BF16, 700, 11, True, 0, False),     # Y = 8192, 2048 keys: one-workgroup order at its limits
+    (16, 32, 9, 64, 4096, 2, synth.FP16, 300, 5, True, 0, False),      # 4096 keys: range-partitioned order
 ]
 
 

@@ -23,9 +23,10 @@ constexpr int64_t kBatchingRangeMaxSlots = 8192;
 struct BatchArgs {
   int64_t Y, chunk;
   int32_t per_layer, L, layer_num;
+  int32_t has_mask, use_layers;  // whether mask / layer_ids hold data (the pointers are always readable)
   const int32_t* expert_ids;
-  const uint8_t* mask;
-  const int32_t* layer_ids;
+  const uint8_t* mask;       // never null: stands in with expert_ids' bytes when there is no mask
+  const int32_t* layer_ids;  // never null: stands in with expert_ids when layers are not used
   const int32_t* session_ids;
   const int32_t* micro_batch_ids;
   const uint8_t* token_data;
@@ -60,17 +61,21 @@ __device__ __forceinline__ const uint8_t* slot_scale(const BatchArgs& a, int64_t
 
 // Slot key: layer * experts_per_layer + expert id; masked slots do not take part, and
 // unmasked slots with an out-of-range expert or layer id are dropped and counted.
+// Every input is loaded unconditionally and the tests combine with bitwise operators: a
+// load behind a test of its pointer, or a short-circuit test, compiles to a branch, and
+// the wait at its end serialised the rounds of a tile (8 rounds: 11 us instead of ~3).
 struct KeyBatching {
   BatchArgs a;
   __device__ uint32_t key(int64_t s, bool& valid, bool& err) const {
-    // every input of the slot is loaded before any decision, so the loads overlap
     const uint32_t c = static_cast<uint32_t>(s) / static_cast<uint32_t>(a.chunk);
-    const uint8_t m = a.mask != nullptr ? a.mask[s] : 0;
-    const int32_t layer = (a.layer_ids != nullptr && a.layer_num >= 1) ? a.layer_ids[c] : 0;
+    const uint8_t m0 = a.mask[s];
+    const int32_t l0 = a.layer_ids[c];
     const int32_t e = a.expert_ids[s];
-    const bool ok = e >= 0 && e < a.per_layer && layer >= 0 && layer < a.L;
-    valid = m == 0 && ok;
-    err = m == 0 && !ok;
+    const bool live = !a.has_mask | (m0 == 0);
+    const int32_t layer = a.use_layers ? l0 : 0;
+    const bool ok = (e >= 0) & (e < a.per_layer) & (layer >= 0) & (layer < a.L);
+    valid = live & ok;
+    err = live & !ok;
     return valid ? static_cast<uint32_t>(layer * a.per_layer + e) : 0u;
   }
 };
@@ -93,19 +98,17 @@ struct RoKeysBatching {
 #pragma unroll
       for (int i = 0; i < kRoVec; ++i) ex[i] = a.expert_ids[min(j0 + i, Y - 1)];
     }
-    uint32_t m[kRoVec] = {0u, 0u, 0u, 0u};
-    if (a.mask != nullptr) {
-      if (full && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
-        const uint32_t q = *reinterpret_cast<const uint32_t*>(a.mask + j0);
+    uint32_t m[kRoVec];
+    if (full && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
+      const uint32_t q = *reinterpret_cast<const uint32_t*>(a.mask + j0);
 #pragma unroll
-        for (int i = 0; i < kRoVec; ++i) m[i] = (q >> (8 * i)) & 0xffu;
-      } else {
+      for (int i = 0; i < kRoVec; ++i) m[i] = a.has_mask ? (q >> (8 * i)) & 0xffu : 0u;
+    } else {
 #pragma unroll
-        for (int i = 0; i < kRoVec; ++i) m[i] = a.mask[min(j0 + i, Y - 1)];
-      }
+      for (int i = 0; i < kRoVec; ++i) m[i] = a.has_mask ? a.mask[min(j0 + i, Y - 1)] : 0u;
     }
-    int32_t layer[kRoVec] = {0, 0, 0, 0};
-    if (a.layer_ids != nullptr && a.layer_num >= 1) {
+    int32_t layer[kRoVec];
+    {
       const uint32_t chunk = static_cast<uint32_t>(a.chunk);
       if (chunk >= kRoVec) {
         const uint32_t jc = min(j0, Y - 1);
@@ -123,10 +126,11 @@ struct RoKeysBatching {
     }
 #pragma unroll
     for (int i = 0; i < kRoVec; ++i) {
-      const bool ok = ex[i] >= 0 && ex[i] < a.per_layer && layer[i] >= 0 && layer[i] < a.L;
-      v[i] = m[i] == 0 && ok;
-      er[i] = m[i] == 0 && !ok;
-      k[i] = v[i] ? static_cast<uint32_t>(layer[i] * a.per_layer + ex[i]) : 0u;
+      const int32_t li = a.use_layers ? layer[i] : 0;
+      const bool ok = (ex[i] >= 0) & (ex[i] < a.per_layer) & (li >= 0) & (li < a.L);
+      v[i] = (m[i] == 0) & ok;
+      er[i] = (m[i] == 0) & !ok;
+      k[i] = v[i] ? static_cast<uint32_t>(li * a.per_layer + ex[i]) : 0u;
     }
   }
 };
@@ -274,17 +278,141 @@ __global__ __launch_bounds__(kRoThreads) void batching_order_kernel(BatchArgs a,
   });
 }
 
+// Slot order in one 1024-thread workgroup, for Y <= 8192 slots and nb <= 2048 keys.
+// Wave w owns the R*64 consecutive slots from w*R*64; every load of a slot (key inputs,
+// its chunk's session and micro-batch ids) is issued in one batch before any use.  The
+// ballot ranking gives each slot's rank among equal keys of its wave (per-wave u16
+// counters in LDS), a prefix over the 16 waves and a scan over the keys give each
+// key's first row and group_list.  The workgroup writes, coalesced, the output row of
+// every slot and its group's first row; the row copy that follows writes the row IDs
+// (from one CU, scattered ID stores took 17 us for 4608 slots).
+// LDS: u16 counters [16][nbp] | u16 totals of each group of 4 waves [4][nbp] | first row
+// of each key [nb].
+constexpr int kWgThreads = 1024;
+constexpr int kWgWaves = kWgThreads / kWave;
+constexpr int64_t kWgMaxSlots = 8192;
+constexpr int kWgMaxKeys = 2048;
+
+template <int R>
+__global__ __launch_bounds__(kWgThreads) void batching_wg_order_kernel(BatchArgs a, int nbits, int nb,
+                                                                      uint32_t* __restrict__ pos_of,
+                                                                      uint32_t* __restrict__ first_of,
+                                                                      int64_t* __restrict__ group_list,
+                                                                      int64_t group_rows, int64_t* __restrict__ actual,
+                                                                      int32_t* __restrict__ err_count) {
+  extern __shared__ uint32_t lds_words[];
+  __shared__ uint32_t wsum[2][2 * kWgWaves + 1];  // ping-pong: a scan's totals are read after it
+  __shared__ uint32_t err_w[kWgWaves];
+  const int nbp = rank_lds_stride(nb);
+  uint16_t* hist = reinterpret_cast<uint16_t*>(lds_words);
+  uint16_t* gsum = hist + kWgWaves * nbp;
+  uint32_t* start = lds_words + (kWgWaves + 4) * nbp / 2;
+  lds_zero_words(lds_words, kWgWaves * nbp / 2);
+  __syncthreads();
+
+  const KeyBatching ks{a};
+  const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
+  const uint32_t lane = lane_id();
+  uint32_t dig[R], rank[R];
+  bool val[R], bad[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
+    const bool in = s < a.Y;
+    bool v = false, e = false;
+    dig[r] = ks.key(in ? s : a.Y - 1, v, e);
+    val[r] = v && in;
+    bad[r] = e && in;
+  }
+  // ballots after every round's loads: a ballot between rounds keeps the next round's
+  // loads from being issued before it
+  uint32_t nerr = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) nerr += static_cast<uint32_t>(__popcll(wave_ballot(bad[r])));
+  rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
+  if (lane == 0) err_w[w] = nerr;
+  __syncthreads();
+  // per key: each wave's base among the key's slots, and the key's total, in two levels
+  // (4 groups of 4 waves, then the groups) so that no thread walks all 16 waves
+  const int kq = threadIdx.x & 255, grp = threadIdx.x >> 8;
+  for (int k = kq; k < nb; k += 256) {
+    uint32_t run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t& h = hist[(4 * grp + i) * nbp + k];
+      const uint32_t c = h;
+      h = static_cast<uint16_t>(run);
+      run += c;
+    }
+    gsum[grp * nbp + k] = static_cast<uint16_t>(run);
+  }
+  __syncthreads();
+  for (int k = kq; k < nb; k += 256) {
+    uint32_t base = 0;
+    for (int i = 0; i < grp; ++i) base += gsum[i * nbp + k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[(4 * grp + i) * nbp + k] += static_cast<uint16_t>(base);
+    if (grp == 3) start[k] = base + gsum[3 * nbp + k];
+  }
+  __syncthreads();
+  // start[k] <- first output row of key k; group_list in the same sweep (one scan of
+  // [counts | presence]: the presence prefix is offset by the counts' total)
+  uint32_t carry = 0, gcarry = 0;
+  for (int k0 = 0, it = 0; k0 < nb; k0 += kWgThreads, it ^= 1) {
+    const int k = k0 + threadIdx.x;
+    const uint32_t cnt = (k < nb) ? start[k] : 0u;
+    uint32_t v[2] = {cnt, cnt > 0 ? 1u : 0u};
+    uint32_t all;
+    block_exscan_multi<kWgThreads, 2>(v, wsum[it], all);
+    const uint32_t tot = wsum[it][kWgWaves];  // sequence 1 starts after all counts
+    if (k < nb) start[k] = carry + v[0];
+    if (cnt > 0) {
+      const int64_t slot = gcarry + v[1] - tot;
+      group_list[2 * slot] = k;
+      group_list[2 * slot + 1] = cnt;
+    }
+    carry += tot;
+    gcarry += all - tot;
+  }
+  for (int64_t g = gcarry + threadIdx.x; g < group_rows; g += kWgThreads) {
+    group_list[2 * g] = 0;
+    group_list[2 * g + 1] = 0;
+  }
+  if (threadIdx.x == 0) {
+    *actual = static_cast<int64_t>(carry);
+    if (err_count != nullptr) {
+      uint32_t e = 0;
+      for (int ww = 0; ww < kWgWaves; ++ww) e += err_w[ww];
+      *err_count = static_cast<int32_t>(e);
+    }
+  }
+  __syncthreads();  // start[] complete
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
+    if (s >= a.Y) continue;
+    const uint32_t first = start[dig[r]];
+    pos_of[s] = val[r] ? first + hist[w * nbp + dig[r]] + rank[r] : kNoRank;
+    first_of[s] = first;
+  }
+}
+
 // Row copy after batching_order_kernel: one wavefront per slot; the INT8 scale moves
 // with its row.
+// With first_of (after batching_wg_order_kernel), lane 0 also writes the row IDs.
 template <int VEC>
-__global__ __launch_bounds__(256) void batching_copy_kernel(BatchArgs a, const uint32_t* __restrict__ pos_of) {
+__global__ __launch_bounds__(256) void batching_copy_kernel(BatchArgs a, const uint32_t* __restrict__ pos_of,
+                                                            const uint32_t* __restrict__ first_of) {
   const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
   if (s >= a.Y) return;
   const uint32_t pos = uniform(pos_of[s]);
   if (pos == kNoRank) return;
   const uint32_t lane = lane_id();
   copy_row<VEC>(slot_row(a, s), a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
-  if (a.dyn_scale != nullptr && lane == 0) a.dyn_scale[pos] = load_scale(slot_scale(a, s));
+  if (lane == 0) {
+    if (first_of != nullptr) write_row_ids(a, s, pos, first_of[s]);  // also moves the scale
+    else if (a.dyn_scale != nullptr) a.dyn_scale[pos] = load_scale(slot_scale(a, s));
+  }
 }
 
 // All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
@@ -308,18 +436,19 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
   const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
   const uint32_t lane = lane_id();
   uint32_t dig[R], rank[R];
-  bool val[R];
-  uint32_t nerr = 0;
+  bool val[R], bad[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
     const bool in = s < a.Y;
     bool v = false, e = false;
-    const uint32_t key = ks.key(in ? s : a.Y - 1, v, e);
-    dig[r] = key;
+    dig[r] = ks.key(in ? s : a.Y - 1, v, e);
     val[r] = v && in;
-    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e && in)));
+    bad[r] = e && in;
   }
+  uint32_t nerr = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) nerr += static_cast<uint32_t>(__popcll(wave_ballot(bad[r])));
   rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
   if (lane == 0) err_w[w] = nerr;
   __syncthreads();
@@ -472,12 +601,14 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p, bool from_conte
   p->small = (p->pass.nt == 1) && p->pass.R == 4 && nb <= 4096 && Y * row <= (int64_t{1} << 22);
   // the slot key reads three inputs, so the one-launch order pays off only for moderate
   // slot counts (measured crossover with the rank / scan / gather path: ~8K slots)
-  p->range_order = !p->small && ro_fits(Y, static_cast<uint64_t>(nb), kBatchingRangeMaxSlots);
+  p->wg_order = !p->small && Y <= kWgMaxSlots && nb <= kWgMaxKeys;
+  p->range_order = !p->small && !p->wg_order && ro_fits(Y, static_cast<uint64_t>(nb), kBatchingRangeMaxSlots);
   if (p->small) {
     p->ws_bytes = 0;
-  } else if (p->range_order) {
+  } else if (p->wg_order || p->range_order) {
     Carve c;
     c.take<uint32_t>(Y);                                              // output row of every slot
+    if (p->wg_order) c.take<uint32_t>(Y);                             // ... and its group's first row
     p->ws_bytes = c.off;
   } else {
     Carve c;
@@ -507,8 +638,11 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   a.per_layer = static_cast<int32_t>(d->expert_num / a.L);
   a.layer_num = static_cast<int32_t>(d->layer_num);
   a.expert_ids = d->expert_ids;
-  a.mask = d->mask;
-  a.layer_ids = d->layer_ids;
+  a.has_mask = d->mask != nullptr;
+  a.use_layers = d->layer_ids != nullptr && d->layer_num >= 1;
+  // absent inputs point at expert_ids (Y readable words, and A <= Y): loads stay unconditional
+  a.mask = a.has_mask ? d->mask : reinterpret_cast<const uint8_t*>(d->expert_ids);
+  a.layer_ids = a.use_layers ? d->layer_ids : d->expert_ids;
   a.session_ids = d->session_ids;
   a.micro_batch_ids = d->micro_batch_ids;
   a.token_data = static_cast<const uint8_t*>(d->token_data);
@@ -539,6 +673,39 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
 
   Carve c;
   c.base = static_cast<char*>(ws);
+  if (p.wg_order) {
+    uint32_t* pos_of = c.take<uint32_t>(p.Y);
+    uint32_t* first_of = c.take<uint32_t>(p.Y);
+    const size_t lds = static_cast<size_t>(kWgWaves + 4) * rank_lds_stride(nb) * sizeof(uint16_t) +
+                       static_cast<size_t>(nb) * sizeof(uint32_t);
+    // as few rounds per wave as the slots need (the ranking's time grows with them)
+    const int rounds = static_cast<int>((p.Y + kWgThreads - 1) / kWgThreads);
+    auto go = [&](auto rc) {
+      constexpr int R = decltype(rc)::value;
+      allow_large_lds(reinterpret_cast<const void*>(&batching_wg_order_kernel<R>), lds);
+      hipLaunchKernelGGL(batching_wg_order_kernel<R>, dim3(1), dim3(kWgThreads), lds, s, a, p.pass.nbits, nb, pos_of,
+                         first_of, d->group_list, d->expert_num, d->actual_token_num, d->err_count);
+    };
+    switch (rounds) {
+      case 1: go(std::integral_constant<int, 1>()); break;
+      case 2: go(std::integral_constant<int, 2>()); break;
+      case 3: go(std::integral_constant<int, 3>()); break;
+      case 4: go(std::integral_constant<int, 4>()); break;
+      case 5: go(std::integral_constant<int, 5>()); break;
+      case 6: go(std::integral_constant<int, 6>()); break;
+      case 7: go(std::integral_constant<int, 7>()); break;
+      default: go(std::integral_constant<int, 8>()); break;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
+    const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+    err = launch_vec(p.vec, [&](auto v) {
+      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of,
+                         first_of);
+    });
+    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+  }
   if (p.range_order) {
     uint32_t* pos_of = c.take<uint32_t>(p.Y);
     const RoPlan rp = ro_plan(static_cast<uint64_t>(nb), kRoGroups);
@@ -550,7 +717,8 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
     if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
     const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
     err = launch_vec(p.vec, [&](auto v) {
-      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of);
+      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of,
+                         static_cast<const uint32_t*>(nullptr));
     });
     if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
     return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;

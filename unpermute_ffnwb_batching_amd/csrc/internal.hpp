@@ -65,6 +65,7 @@ struct BatchingPlan {
   const uint8_t* scale_base = nullptr;
   int64_t scale_stride = 0;
   bool small = false;  // single fused workgroup
+  bool wg_order = false;     // slot order in one 1024-thread workgroup, then a row copy
   bool range_order = false;  // slot order in one range-partitioned launch, then a row copy
   SortPass pass;
   int vec = 16;        // row copy width class: 16, 4 or 1

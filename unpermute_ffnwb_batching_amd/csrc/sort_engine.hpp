@@ -162,8 +162,7 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
   const int64_t base = static_cast<int64_t>(blockIdx.x) * (kRankThreads * R) + static_cast<int64_t>(w) * (kWave * R);
   const uint32_t dmask = (nbits >= 32) ? ~0u : ((1u << nbits) - 1u);
   uint32_t dig[R], rank[R];
-  bool val[R];
-  uint32_t nerr = 0;
+  bool val[R], bad[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t j = base + r * kWave + lane;
@@ -172,8 +171,13 @@ __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t 
     const uint32_t key = ks.key(in ? j : n - 1, v, e);
     dig[r] = (key >> shift) & dmask;
     val[r] = v && in;
-    nerr += static_cast<uint32_t>(__popcll(wave_ballot(e && in)));
+    bad[r] = e && in;
   }
+  // the ballots come after every round's loads: a ballot between rounds keeps the next
+  // round's loads from being issued before it
+  uint32_t nerr = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) nerr += static_cast<uint32_t>(__popcll(wave_ballot(bad[r])));
   rank_rounds<R>(dig, val, nbits, hist + w * nbp, rank);
   if (lane == 0) err_w[w] = nerr;
   __syncthreads();
