@@ -12,9 +12,12 @@ byte the operations need, read once, plus every output byte, written once) divid
 the measured step time.  Inputs are resident in HBM before timing; the step's working
 set (~2 GB) is far above the 256 MB Infinity Cache, so steps do not hit in it.
 
-Also reported: per-workload times with the caches flushed between iterations, the
-roofline of the dominant kernel (the non-padded gather-reduce, timed with HIP events
-on its own stream position), and the CPU oracle timed on the host.
+Also reported, per workload: the median, p10 and p90 call time with L2 and the
+Infinity Cache flushed (a 1 GiB write) before every iteration, the warm back-to-back
+time, and a plain device copy moving the same number of bytes (what a streaming kernel
+reaches); the roofline of the dominant kernel (the non-padded gather-reduce, timed with
+HIP events on its own stream position); and the CPU oracle timed on the host (median of
+3 runs per workload).
 """
 
 import argparse
@@ -41,12 +44,60 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--detail-iters", type=int, default=20, help="per-workload timed iterations (0 = skip)")
+    ap.add_argument("--detail-iters", type=int, default=100, help="per-workload timed iterations (0 = skip)")
+    ap.add_argument("--no-next-rows", action="store_true", help="skip the measurements outside the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of workloads to keep (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- timing helpers
+
+_FLUSH = []
+
+
+def flushed_times(run, stream, iters):
+    """Call times (ms) of run(stream), L2 and the 256 MB Infinity Cache flushed by a 1 GiB
+    write before each call (outside the timed bracket)."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(1 << 30, dtype=torch.uint8, device="cuda"))
+    flush = _FLUSH[0]
+    ts = []
+    for _ in range(iters):
+        flush.fill_(1)
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record(stream)
+        run(stream)
+        e.record(stream)
+        e.synchronize()
+        ts.append(b.elapsed_time(e))
+    return np.array(ts)
+
+
+def warm_ms(run, stream, iters):
+    """Mean time (ms) of back-to-back calls."""
+    import torch
+    b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record(stream)
+    for _ in range(iters):
+        run(stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return b.elapsed_time(e) / iters
+
+
+def copy_gbps(nbytes, stream, iters):
+    """A plain device copy whose reads plus writes equal nbytes, flushed like the calls."""
+    import torch
+    n = max(int(nbytes) // 2, 1)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ts = flushed_times(lambda st: dst.copy_(src), stream, iters)
+    del src, dst
+    return round(2 * n / float(np.median(ts)) / 1e6, 1)
 
 
 # ----------------------------------------------------------------------------- algorithmic bytes
@@ -143,17 +194,7 @@ def measure_skip(args, stream, c):
            "rows_valid": nval, "rows_read": nread, "alg_bytes": alg,
            "us_per_call": round(call_ms * 1e3, 2), "GBps": round(alg / call_ms / 1e6, 1)}
     if args.detail_iters > 0:
-        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
-        ts = []
-        for _ in range(args.detail_iters):
-            flush.fill_(1)
-            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            call.run(stream)
-            e.record(stream)
-            e.synchronize()
-            ts.append(b.elapsed_time(e))
-        del flush
+        ts = flushed_times(call.run, stream, args.detail_iters)
         res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
     if not args.no_cpu_baseline:
         from _gpu import oracle_unpermute, check_unpermute
@@ -203,17 +244,7 @@ def measure_ctx(args, stream):
            "rows": actual, "alg_bytes": alg, "us_per_call": round(call_ms * 1e3, 2),
            "GBps": round(alg / call_ms / 1e6, 1)}
     if args.detail_iters > 0:
-        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
-        ts = []
-        for _ in range(args.detail_iters):
-            flush.fill_(1)
-            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            call.run(stream)
-            e.record(stream)
-            e.synchronize()
-            ts.append(b.elapsed_time(e))
-        del flush
+        ts = flushed_times(call.run, stream, args.detail_iters)
         res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
     if not args.no_cpu_baseline:
         from _gpu import oracle_ctx, check_ctx
@@ -297,17 +328,7 @@ def measure_permute(args, stream):
            "copy_kernel_us": round(copy_ms * 1e3, 2),
            "copy_kernel_GBps": round((alg - c["T"] * c["E"]) / copy_ms / 1e6, 1)}
     if args.detail_iters > 0:
-        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
-        ts = []
-        for _ in range(args.detail_iters):
-            flush.fill_(1)
-            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            call.run(stream)
-            e.record(stream)
-            e.synchronize()
-            ts.append(b.elapsed_time(e))
-        del flush
+        ts = flushed_times(call.run, stream, args.detail_iters)
         res["us_median_flushed"] = round(float(np.median(ts)) * 1e3, 2)
     if not args.no_cpu_baseline:
         from _gpu import oracle_permute, check_permute
@@ -448,27 +469,23 @@ def main():
     torch.cuda.synchronize()
     ms_nohook = s2.elapsed_time(e2) / K
 
-    # per-workload timing with L2 / Infinity Cache flushed before every iteration
+    # per workload: flushed-cache times (10 warm-ups first), the warm back-to-back time,
+    # and a plain copy of the same byte count for context
     detail = {}
     if args.detail_iters > 0:
-        flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
         for n, call in calls.items():
-            ts = []
-            for _ in range(args.detail_iters):
-                flush.fill_(1)
-                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                b.record(stream)
+            for _ in range(10):
                 call.run(stream)
-                e.record(stream)
-                e.synchronize()
-                ts.append(b.elapsed_time(e))
+            ts = flushed_times(call.run, stream, args.detail_iters)
             med = float(np.median(ts))
+            warm = warm_ms(call.run, stream, 20)
             detail[n] = {"us_median": round(med * 1e3, 2), "us_p10": round(float(np.percentile(ts, 10)) * 1e3, 2),
-                         "us_p90": round(float(np.percentile(ts, 90)) * 1e3, 2),
+                         "us_p90": round(float(np.percentile(ts, 90)) * 1e3, 2), "iters": args.detail_iters,
                          "alg_bytes": alg[n], "GBps": round(alg[n] / med / 1e6, 1),
                          "pct_hbm_peak": round(100 * alg[n] / med / 1e6 / HBM_PEAK_GBS, 1),
-                         "rows_per_s": round(rows[n] / med * 1e3, 1)}
-        del flush
+                         "rows_per_s": round(rows[n] / med * 1e3, 1),
+                         "us_warm": round(warm * 1e3, 2), "GBps_warm": round(alg[n] / warm / 1e6, 1),
+                         "copy_same_bytes_GBps": copy_gbps(alg[n], stream, 20)}
 
     # parity of the timed outputs and the CPU oracle baseline, on the host
     parity = None
@@ -478,14 +495,18 @@ def main():
         t_or = {}
         refs = {}
         for n, c in cases.items():
-            t1 = time.perf_counter()
-            refs[n] = oracle_batching(c) if n.startswith("batching") else oracle_unpermute(c)
-            t_or[n] = time.perf_counter() - t1
+            runs = []
+            for _ in range(3):
+                t1 = time.perf_counter()
+                refs[n] = oracle_batching(c) if n.startswith("batching") else oracle_unpermute(c)
+                runs.append(time.perf_counter() - t1)
+            t_or[n] = float(np.median(runs))
         secs = sum(t_or.values())
         cpu = {"value": round(step_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "one full step (all four workloads) through the NumPy oracle, single-threaded; "
-                         f"{secs:.1f} s on {os.cpu_count()} visible host cores",
-               "seconds_per_workload": {n: round(v, 3) for n, v in t_or.items()}}
+               "sample": "one full step (all four workloads) through the NumPy oracle, single-threaded, median "
+                         f"of 3 runs per workload; {secs:.1f} s on {os.cpu_count()} visible host cores",
+               "per_workload": {n: {"s": round(v, 3), "GBps": round(alg[n] / v / 1e9, 4),
+                                    "rows_per_s": round(rows[n] / v, 1)} for n, v in t_or.items()}}
         parity = True
         for n, c in cases.items():
             try:
@@ -508,13 +529,15 @@ def main():
                 "alg_bytes_per_launch": red_bytes, "avg_launch_us": round(hot_ms * 1e3, 2)}
 
     next_rows = {}
-    if not args.only or "permute" in args.only.split(","):
+    if args.no_next_rows:
+        pass
+    elif not args.only or "permute" in args.only.split(","):
         next_rows["moe_permute_nonpadded"] = measure_permute(args, stream)
-    if not args.only or "context" in args.only.split(","):
+    if not args.no_next_rows and (not args.only or "context" in args.only.split(",")):
         next_rows["batching_from_context"] = measure_ctx(args, stream)
-    if not args.only or "update_expert" in args.only.split(","):
+    if not args.no_next_rows and (not args.only or "update_expert" in args.only.split(",")):
         next_rows["moe_update_expert"] = measure_update_expert(args, stream)
-    if "unpermute_padded" in cases:
+    if not args.no_next_rows and "unpermute_padded" in cases:
         next_rows["unpermute_padded_skip_zero_weight"] = measure_skip(args, stream, cases["unpermute_padded"])
     next_rows = next_rows or None
 
