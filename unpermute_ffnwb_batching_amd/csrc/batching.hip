@@ -43,6 +43,13 @@ struct BatchArgs {
   const uint64_t* chunk_src;  // context mode: address of each chunk's first row, else nullptr
 };
 
+// A device address as a pointer into global memory: made in the global address space,
+// so that the compiler keeps global (not flat) loads for everything derived from it.
+typedef const __attribute__((address_space(1))) uint8_t* GlobalBytes;
+__device__ __forceinline__ const uint8_t* global_bytes(uint64_t addr) {
+  return (const uint8_t*)((GlobalBytes)addr);
+}
+
 // Source row of slot s: token_data + s * stride, or in context mode entry s % chunk of
 // chunk s / chunk, whose rows start at chunk_src[chunk] (the branch is uniform).
 __device__ __forceinline__ const uint8_t* slot_row(const BatchArgs& a, int64_t s) {
@@ -50,7 +57,7 @@ __device__ __forceinline__ const uint8_t* slot_row(const BatchArgs& a, int64_t s
   const uint32_t chunk = static_cast<uint32_t>(a.chunk);
   const uint32_t c = static_cast<uint32_t>(s) / chunk;
   const uint32_t j = static_cast<uint32_t>(s) - c * chunk;
-  return reinterpret_cast<const uint8_t*>(a.chunk_src[c]) + static_cast<int64_t>(j) * a.stride;
+  return global_bytes(a.chunk_src[c]) + static_cast<int64_t>(j) * a.stride;
 }
 
 // INT8 dynamic scale of slot s; in context mode packed after the row's H bytes.
