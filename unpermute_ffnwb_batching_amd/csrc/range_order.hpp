@@ -167,19 +167,27 @@ __device__ __forceinline__ uint32_t ro_middle(uint32_t* cnt, uint32_t kr, uint32
                                               uint32_t& key_count, uint32_t& end) {
   __syncthreads();
   const uint32_t k = threadIdx.x;
+  // all 16 counters are read before any is written back: with kr unknown at compile
+  // time, a read-modify-write per wave could not be reordered and cost 16 serial LDS
+  // round trips per key, twice
+  uint32_t pre[kRoWaves];
   uint32_t tot = 0;
   if (k < kr) {
+    uint32_t c[kRoWaves];
+#pragma unroll
+    for (int w = 0; w < kRoWaves; ++w) c[w] = cnt[w * kr + k];
+#pragma unroll
     for (int w = 0; w < kRoWaves; ++w) {
-      const uint32_t c = cnt[w * kr + k];
-      cnt[w * kr + k] = tot;
-      tot += c;
+      pre[w] = tot;
+      tot += c[w];
     }
   }
   // sequence 0: lanes' below counts, sequence 1: key totals -> v[1] = first position of key k
   uint32_t v[2] = {below, tot};
   block_exscan_multi<kRoThreads, 2>(v, wsum, end);
   if (k < kr) {
-    for (int w = 0; w < kRoWaves; ++w) cnt[w * kr + k] += v[1];
+#pragma unroll
+    for (int w = 0; w < kRoWaves; ++w) cnt[w * kr + k] = pre[w] + v[1];
   }
   __syncthreads();
   key_count = tot;
