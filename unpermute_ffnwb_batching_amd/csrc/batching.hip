@@ -341,25 +341,42 @@ __global__ __launch_bounds__(kWgThreads) void batching_wg_order_kernel(BatchArgs
   __syncthreads();
   // per key: each wave's base among the key's slots, and the key's total, in two levels
   // (4 groups of 4 waves, then the groups) so that no thread walks all 16 waves
+  // (counters are read into registers before anything is written back: with the row
+  // pitch nbp a runtime value, the compiler cannot reorder a read-modify-write sequence)
   const int kq = threadIdx.x & 255, grp = threadIdx.x >> 8;
-  for (int k = kq; k < nb; k += 256) {
-    uint32_t run = 0;
+  constexpr int kPasses = kWgMaxKeys / 256;
+  uint32_t pre[kPasses][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t& h = hist[(4 * grp + i) * nbp + k];
-      const uint32_t c = h;
-      h = static_cast<uint16_t>(run);
-      run += c;
+  for (int m = 0; m < kPasses; ++m) {
+    const int k = kq + m * 256;
+    if (k < nb) {
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = hist[(4 * grp + i) * nbp + k];
+      uint32_t run = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pre[m][i] = run;
+        run += c[i];
+      }
+      gsum[grp * nbp + k] = static_cast<uint16_t>(run);
     }
-    gsum[grp * nbp + k] = static_cast<uint16_t>(run);
   }
   __syncthreads();
-  for (int k = kq; k < nb; k += 256) {
-    uint32_t base = 0;
-    for (int i = 0; i < grp; ++i) base += gsum[i * nbp + k];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hist[(4 * grp + i) * nbp + k] += static_cast<uint16_t>(base);
-    if (grp == 3) start[k] = base + gsum[3 * nbp + k];
+  for (int m = 0; m < kPasses; ++m) {
+    const int k = kq + m * 256;
+    if (k < nb) {
+      uint32_t g[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = gsum[i * nbp + k];
+      uint32_t base = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base += i < grp ? g[i] : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[(4 * grp + i) * nbp + k] = static_cast<uint16_t>(pre[m][i] + base);
+      if (grp == 3) start[k] = base + g[3];
+    }
   }
   __syncthreads();
   // start[k] <- first output row of key k; group_list in the same sweep (one scan of
