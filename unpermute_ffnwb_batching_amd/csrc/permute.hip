@@ -31,13 +31,43 @@
 
 namespace ffnwb {
 
-constexpr int kPermuteThreads = 512;
+constexpr int kPermuteThreads = 1024;
 constexpr int kPermuteMaxExperts = 256;
 
 // LDS bytes of permute_order_kernel.
 inline size_t permute_order_lds_bytes(int ntiles, int E, bool padded) {
   const size_t words = static_cast<size_t>(ntiles) * E + static_cast<size_t>(kMaskGroups) * E + 2 * static_cast<size_t>(E);
   return words * sizeof(uint32_t) + (padded ? 0 : static_cast<size_t>(kMaskRows) * E);
+}
+
+// Places the non-zero entries of NR consecutive rows (rows rbase .. rbase+NR-1 of group g)
+// of one work item, in row order, from the running offsets off[w] of its W columns.
+template <int W, bool PADDED, int NR>
+__device__ __forceinline__ void permute_place_rows(const uint32_t (&xr)[NR], int rbase, int g, int c, int64_t t0,
+                                                   int64_t T, int32_t E, const uint32_t* base, uint32_t (&off)[W],
+                                                   int64_t N, int64_t C, int32_t* __restrict__ source_of,
+                                                   int32_t* __restrict__ sorted_indices, uint8_t* inoff) {
+  const int64_t r0 = t0 + g * kMaskGroupRows + rbase;
+  uint32_t bs[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) bs[w] = base[c * W + w];  // read once, outside the per-entry branches
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      if (r0 + r < T && ((xr[r] >> (8 * w)) & 0xffu) != 0) {
+        const int e = c * W + w;
+        const uint32_t place = bs[w] + off[w];
+        if (PADDED) {
+          if (place < static_cast<uint64_t>(C)) sorted_indices[e * C + place] = static_cast<int32_t>(r0 + r);
+        } else {
+          if (place < static_cast<uint64_t>(N)) source_of[place] = static_cast<int32_t>(r0 + r);
+          inoff[(g * kMaskGroupRows + rbase + r) * E + e] = static_cast<uint8_t>(off[w]);
+        }
+        ++off[w];
+      }
+    }
+  }
 }
 
 template <int W, bool PADDED>
@@ -109,32 +139,45 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
     }
   }
   __syncthreads();
-  // 3. a place for every entry of the tile, rows in order within each item
-  for (int it = tid; it < items; it += NT) {
-    const int g = it / cu;
-    const int c = it - g * cu;
-    const int64_t r0 = t0 + g * kMaskGroupRows;
-    uint32_t x[kMaskGroupRows], cnt[W];
-    mask_item_counts<W>(map, T, E, r0, c, x, cnt);
+  // 3. a place for every entry of the tile, rows in order within each item; when the
+  //    workgroup has twice as many threads as items, two adjacent lanes share an item (8
+  //    rows each, the second starting after the first's counts)
+  if (2 * items <= NT) {
+    constexpr int kHalf = kMaskGroupRows / 2;
+    const int it = tid >> 1, hf = tid & 1;
+    const bool act = it < items;
+    const int g = act ? it / cu : 0;
+    const int c = act ? it - g * cu : 0;
+    const int64_t r0 = t0 + g * kMaskGroupRows + hf * kHalf;
+    uint32_t x[kHalf], cnt[W];
+#pragma unroll
+    for (int r = 0; r < kHalf; ++r) x[r] = load_map_unit<W>(map + min(r0 + r, T - 1) * E + c * W);  // clamped
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      cnt[w] = 0u;
+#pragma unroll
+      for (int r = 0; r < kHalf; ++r) cnt[w] += (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
+    }
     uint32_t off[W];
 #pragma unroll
-    for (int w = 0; w < W; ++w) off[w] = gc[g * E + c * W + w];
+    for (int w = 0; w < W; ++w) {
+      const uint32_t first_half = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cnt[w]), 1));
+      off[w] = (act ? gc[g * E + c * W + w] : 0u) + (hf ? first_half : 0u);
+    }
+    if (act)
+      permute_place_rows<W, PADDED, kHalf>(x, hf * kHalf, g, c, t0, T, E, base, off, N, C, source_of, sorted_indices,
+                                           inoff);
+  } else {
+    for (int it = tid; it < items; it += NT) {
+      const int g = it / cu;
+      const int c = it - g * cu;
+      uint32_t x[kMaskGroupRows], cnt[W];
+      mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
+      uint32_t off[W];
 #pragma unroll
-    for (int r = 0; r < kMaskGroupRows; ++r) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        if (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) {
-          const int e = c * W + w;
-          const uint32_t place = base[e] + off[w];
-          if (PADDED) {
-            if (place < static_cast<uint64_t>(C)) sorted_indices[e * C + place] = static_cast<int32_t>(r0 + r);
-          } else {
-            if (place < static_cast<uint64_t>(N)) source_of[place] = static_cast<int32_t>(r0 + r);
-            inoff[(g * kMaskGroupRows + r) * E + e] = static_cast<uint8_t>(off[w]);
-          }
-          ++off[w];
-        }
-      }
+      for (int w = 0; w < W; ++w) off[w] = gc[g * E + c * W + w];
+      permute_place_rows<W, PADDED, kMaskGroupRows>(x, 0, g, c, t0, T, E, base, off, N, C, source_of,
+                                                    sorted_indices, inoff);
     }
   }
   if (PADDED) {
@@ -147,25 +190,52 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
     return;
   }
   __syncthreads();
-  // 4. the slots of each token of the tile: its entries in ascending expert order
-  for (int rr = tid; rr < kMaskRows; rr += NT) {
-    const int64_t t = t0 + rr;
-    if (t >= T) break;
-    const uint8_t* row = map + t * E;
-    int32_t k = 0;
-    for (int c0 = 0; c0 < cu; c0 += 16) {
-      uint32_t x[16];
+  // 4. the slots of each token of the tile: its entries in ascending expert order.  A
+  //    token's map row is spread over lanes (one map unit each) and each entry's slot k
+  //    comes from ballots: the non-zero entries of lower lanes plus the lane's earlier
+  //    ones.  (One thread per token walking its row serially took half the kernel.)
+  {
+    const uint32_t lane = lane_id();
+    const int wv = tid / kWave;
+    constexpr int NW = NT / kWave;
+    if (cu <= 32) {
+      // two tokens per wave iteration: lanes [0, 32) and [32, 64); every map load of the
+      // wave's tokens is issued before the first is used
+      constexpr int kIters = kMaskRows / (2 * NW);
+      const int sub = static_cast<int>(lane >> 5);
+      const int ul = static_cast<int>(lane & 31u);
+      const uint64_t half = sub ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+      uint32_t xs[kIters];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = load_map_unit<W>(row + min(c0 + u, cu - 1) * W);  // clamped
+      for (int i = 0; i < kIters; ++i) {
+        const int64_t t = min(t0 + (wv * kIters + i) * 2 + sub, T - 1);
+        xs[i] = load_map_unit<W>(map + t * E + min(ul, cu - 1) * W);  // clamped
+      }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (c0 + u >= cu) continue;
+      for (int i = 0; i < kIters; ++i) {
+        const int rr = (wv * kIters + i) * 2 + sub;
+        const int64_t t = t0 + rr;
+        const bool uok = t < T && ul < cu;
+        uint32_t f[W], below = 0, total = 0;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-          if (((x[u] >> (8 * w)) & 0xffu) != 0) {
-            const int e = (c0 + u) * W + w;
-            const uint32_t r = base[e] + inoff[rr * E + e];
-            if (k < K) {
+          f[w] = (uok && ((xs[i] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
+          const uint64_t m = wave_ballot(f[w] != 0) & half;
+          below += count_below(m);
+          total += static_cast<uint32_t>(__popcll(m));
+        }
+        // the lane's row places, read outside the per-entry branches (a lane's W experts
+        // are adjacent: one read of base, one of the in-tile offsets)
+        const int ue = min(ul, cu - 1) * W;
+        uint32_t rp[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) rp[w] = base[ue + w] + inoff[rr * E + ue + w];
+        uint32_t k = below;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          if (f[w]) {
+            const uint32_t r = rp[w];
+            if (k < static_cast<uint32_t>(K)) {
               sorted_indices[t * K + k] = (r < static_cast<uint64_t>(N)) ? static_cast<int32_t>(r) : -1;
             } else if (r < static_cast<uint64_t>(N)) {
               source_of[r] = -static_cast<int32_t>(t) - 2;  // a row no slot lists (token beyond topK)
@@ -173,9 +243,48 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
             ++k;
           }
         }
+        if (t < T)
+          for (int q = static_cast<int>(total) + ul; q < K; q += 32) sorted_indices[t * K + q] = -1;
+      }
+    } else {
+      // one token per wave iteration, its map units 64 at a time
+      for (int rr = wv; rr < kMaskRows; rr += NW) {
+        const int64_t t = t0 + rr;
+        if (t >= T) break;  // uniform
+        uint32_t k0 = 0;
+        for (int c0 = 0; c0 < cu; c0 += kWave) {
+          const int u = c0 + static_cast<int>(lane);
+          const uint32_t x = load_map_unit<W>(map + t * E + min(u, cu - 1) * W);  // clamped
+          uint32_t f[W], below = 0, total = 0;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            f[w] = (u < cu && ((x >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
+            const uint64_t m = wave_ballot(f[w] != 0);
+            below += count_below(m);
+            total += static_cast<uint32_t>(__popcll(m));
+          }
+          const int ue = min(u, cu - 1) * W;
+          uint32_t rp[W];
+#pragma unroll
+          for (int w = 0; w < W; ++w) rp[w] = base[ue + w] + inoff[rr * E + ue + w];
+          uint32_t k = k0 + below;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            if (f[w]) {
+              const uint32_t r = rp[w];
+              if (k < static_cast<uint32_t>(K)) {
+                sorted_indices[t * K + k] = (r < static_cast<uint64_t>(N)) ? static_cast<int32_t>(r) : -1;
+              } else if (r < static_cast<uint64_t>(N)) {
+                source_of[r] = -static_cast<int32_t>(t) - 2;
+              }
+              ++k;
+            }
+          }
+          k0 += total;
+        }
+        for (int q = static_cast<int>(k0 + lane); q < K; q += kWave) sorted_indices[t * K + q] = -1;
       }
     }
-    for (; k < K; ++k) sorted_indices[t * K + k] = -1;
   }
   // 5. rows past the non-zero entries have no source
   for (int64_t r = static_cast<int64_t>(tile) * NT + tid; r < N; r += static_cast<int64_t>(gridDim.x) * NT)
