@@ -29,6 +29,7 @@ NONPAD = [
     (50, 6, 1, 64, synth.FP32, None, 60, False, "slots"),              # branch 4, no probs
     (3000, 8, 64, 32, synth.BF16, synth.FP32, 2000, True, "compact"),  # aux order needs 2 LSD passes
     (40000, 8, 64, 16, synth.BF16, synth.FP32, 30000, True, "compact"),  # 320000 slots
+    (20000, 4, 129, 16, synth.BF16, synth.FP32, 5000, True, "compact"),  # 79 tiles x 17 column ranges
     (2, 512, 600, 16, synth.FP16, synth.FP16, 100, True, "slots"),    # topK = 512
     (1000, 2, 300, 264, synth.FP32, synth.FP32, 0, True, "compact"),
 ]

@@ -26,6 +26,13 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m) {
 
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
 
+// Sum of one value per lane over the calling wave; every lane receives it.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
 template <typename T>
 __device__ __forceinline__ T uniform(T v) {
   return static_cast<T>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));

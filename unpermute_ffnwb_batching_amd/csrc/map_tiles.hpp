@@ -2,7 +2,9 @@
 // kMaskRows token rows; a work item is kMaskGroupRows consecutive rows x W consecutive
 // columns (W = 4 when the columns come in aligned groups of 4, else 1), read as one
 // W-byte load per row.  mask_tile_count_kernel writes hist[tile*E + e], the non-zero
-// entries of column e in the tile.
+// entries of column e in the tile.  Its workgroups split each tile by column ranges of
+// kMaskRangeUnits work-item columns, one item per thread, so that a map of a few MB is
+// read by several times more compute units than there are tiles.
 #pragma once
 
 #include "device_common.hpp"
@@ -37,25 +39,48 @@ __device__ __forceinline__ void mask_item_counts(const uint8_t* __restrict__ map
   }
 }
 
+constexpr int kMaskRangeUnits = 8;                                // work-item columns per range
+constexpr int kMaskSplitThreads = kMaskGroups * kMaskRangeUnits;   // 128: one item per thread
+
+// Column ranges of a map with E columns read W at a time.
+__host__ __device__ inline int mask_ranges(int32_t E, int W) {
+  return (E / W + kMaskRangeUnits - 1) / kMaskRangeUnits;
+}
+
+// Grid (tiles, mask_ranges(E, W)) of kMaskSplitThreads threads.  Thread i takes row group
+// i / kMaskRangeUnits and work-item column i % kMaskRangeUnits of its range.  With
+// range_tot given, range_tot[tile * ranges + r] = the range's non-zero entries in the tile.
 template <int W>
-__global__ __launch_bounds__(256) void mask_tile_count_kernel(const uint8_t* __restrict__ map, int64_t T, int32_t E,
-                                                              uint32_t* __restrict__ hist) {
-  extern __shared__ uint32_t colc[];  // [E]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) colc[e] = 0u;
+__global__ __launch_bounds__(kMaskSplitThreads) void mask_tile_count_kernel(const uint8_t* __restrict__ map,
+                                                                            int64_t T, int32_t E,
+                                                                            uint32_t* __restrict__ hist,
+                                                                            uint32_t* __restrict__ range_tot) {
+  __shared__ uint32_t colc[kMaskRangeUnits * W];
+  const int tid = threadIdx.x;
+  const int u0 = blockIdx.y * kMaskRangeUnits;
+  const int nu = min(kMaskRangeUnits, E / W - u0);
+  const int ncols = nu * W;
+  const int g = tid / kMaskRangeUnits, u = tid % kMaskRangeUnits;
+  const bool act = u < nu;
+  uint32_t x[kMaskGroupRows], cnt[W];
+  mask_item_counts<W>(map, T, E, static_cast<int64_t>(blockIdx.x) * kMaskRows + g * kMaskGroupRows,
+                      u0 + (act ? u : 0), x, cnt);
+  if (tid < ncols) colc[tid] = 0u;
   __syncthreads();
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskRows;
-  const int cu = E / W;
-  for (int it = threadIdx.x; it < kMaskGroups * cu; it += blockDim.x) {
-    const int g = it / cu;
-    const int c = it - g * cu;
-    uint32_t x[kMaskGroupRows], cnt[W];
-    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
+  if (act) {
 #pragma unroll
     for (int w = 0; w < W; ++w)
-      if (cnt[w] != 0) atomicAdd(&colc[c * W + w], cnt[w]);
+      if (cnt[w] != 0) atomicAdd(&colc[u * W + w], cnt[w]);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = colc[e];
+  if (tid < kWave) {  // ncols <= 32: one wave writes the range
+    const uint32_t v = tid < ncols ? colc[tid] : 0u;
+    if (tid < ncols) hist[static_cast<int64_t>(blockIdx.x) * E + u0 * W + tid] = v;
+    if (range_tot != nullptr) {
+      const uint32_t sum = wave_sum(v);
+      if (tid == 0) range_tot[static_cast<int64_t>(blockIdx.x) * gridDim.y + blockIdx.y] = sum;
+    }
+  }
 }
 
 }  // namespace ffnwb

@@ -452,13 +452,13 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   const int32_t E = static_cast<int32_t>(p.E);
   const int nt = static_cast<int>(p.ntiles);
   const bool wide = E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0;
-  const size_t count_lds = static_cast<size_t>(E) * sizeof(uint32_t);
   const size_t lds = permute_order_lds_bytes(nt, E, p.padded);
   auto go = [&](auto wtag, auto ptag) {
     constexpr int W = decltype(wtag)::value;
     constexpr bool PADDED = decltype(ptag)::value;
     allow_large_lds(reinterpret_cast<const void*>(&permute_order_kernel<W, PADDED>), lds);
-    hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt), dim3(256), count_lds, s, map, p.T, E, hist);
+    hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt, mask_ranges(E, W)), dim3(kMaskSplitThreads), 0, s, map,
+                       p.T, E, hist, static_cast<uint32_t*>(nullptr));
     hipLaunchKernelGGL((permute_order_kernel<W, PADDED>), dim3(nt), dim3(kPermuteThreads), lds, s, map, p.T, E, nt,
                        hist, p.N, static_cast<int32_t>(p.K), d->capacity, source_of, d->sorted_indices);
   };

@@ -16,6 +16,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -83,16 +84,22 @@ __global__ __launch_bounds__(256) void mask_scatter_kernel(const uint8_t* __rest
     if (g >= filled) pp[g] = P(0);
 }
 
-// Probs compaction in two launches, for maps whose tile histogram fits LDS.  Tiles of
-// kMaskRows token rows; a work item is kMaskGroupRows consecutive rows x W consecutive
-// columns (W = 4 when the columns come in aligned groups of 4, else 1), read as one
-// W-byte map load and one W-element probs load per row.
-//   mask_tile_count_kernel   hist[tile*E + e] = non-zero entries of column e in the tile;
-//   mask_compact_kernel      each tile's workgroup copies the whole histogram to LDS,
-//                            derives the column totals, the column starts (one scan over
-//                            the columns) and its own tile prefix, then the start of each
-//                            of its row groups, and places its entries in row order.
-// No scan launch: the histogram is small enough for every workgroup to read it.
+// Probs compaction in two launches, for maps whose tile histogram is small (at most
+// kMaskLdsHist words).  Tiles of kMaskRows token rows; a work item is kMaskGroupRows
+// consecutive rows x W consecutive columns (W = 4 when the columns come in aligned groups
+// of 4, else 1), read as one W-byte map load and one W-element probs load per row.  Both
+// launches run on the grid (tiles, column ranges of kMaskRangeUnits work-item columns).
+//   mask_tile_count_kernel  hist[tile*E + e] = non-zero entries of column e in the tile,
+//                           range_tot[tile*ranges + r] = those of range r;
+//   mask_compact_kernel     workgroup (tile, r): its first column starts after the
+//                           entries of all lower ranges (their range totals over all
+//                           tiles), each further column after the lower columns of the
+//                           range (their totals over all tiles); the column's counts in
+//                           earlier tiles give the start of the tile's run in each
+//                           column; the items stage their entries in LDS (row order within
+//                           each column, no branch per entry), and the runs are copied out
+//                           with consecutive stores.
+// No scan launch: every workgroup reads the histogram words of its own columns only.
 template <int W, typename P>
 struct ProbUnit {
   P v[W];
@@ -110,13 +117,6 @@ struct ProbUnit {
     }
   }
 };
-
-// LDS words of mask_compact_kernel.
-inline size_t mask_compact_lds_words(int ntiles, int E) {
-  return static_cast<size_t>(ntiles) * E + static_cast<size_t>(kMaskGroups) * E + 2 * static_cast<size_t>(E);
-}
-
-constexpr int kMaskCompactThreads = 512;
 
 // One work item's map units and probs, loaded before they are needed.
 template <int W, typename P>
@@ -141,120 +141,174 @@ struct MaskItem {
       for (int w = 0; w < W; ++w) cnt[w] += (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) ? 1u : 0u;
     }
   }
-  // writes the item's non-zero entries from positions pos[w] on, rows in order
-  __device__ __forceinline__ void place(int64_t T, int64_t r0, uint32_t (&pos)[W], P* __restrict__ pp,
-                                        int64_t N) const {
+  // stages every entry of the item in LDS without a branch: a non-zero entry of column w
+  // goes to slot sp[w] (then the next one) with its output position gp[w] (then the next
+  // one), any other entry to the lane's trash slot
+  __device__ __forceinline__ void stage(int64_t T, int64_t r0, uint32_t (&sp)[W], uint32_t (&gp)[W],
+                                        uint2* __restrict__ st, uint32_t trash) const {
 #pragma unroll
     for (int r = 0; r < kMaskGroupRows; ++r) {
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        if (r0 + r < T && ((x[r] >> (8 * w)) & 0xffu) != 0) {
-          if (pos[w] < N) pp[pos[w]] = pv[r].v[w];
-          ++pos[w];
-        }
+        const bool nz = (r0 + r < T) & (((x[r] >> (8 * w)) & 0xffu) != 0);
+        st[nz ? sp[w] : trash] = make_uint2(static_cast<uint32_t>(pv[r].v[w]), gp[w]);
+        sp[w] += nz ? 1u : 0u;
+        gp[w] += nz ? 1u : 0u;
       }
     }
   }
 };
 
 template <int W, typename P>
-__global__ __launch_bounds__(kMaskCompactThreads) void mask_compact_kernel(const uint8_t* __restrict__ map,
-                                                                           const P* __restrict__ probs, int64_t T,
-                                                                           int32_t E, int ntiles,
-                                                                           const uint32_t* __restrict__ hist,
-                                                                           P* __restrict__ pp, int64_t N) {
-  constexpr int NT = kMaskCompactThreads;
-  extern __shared__ uint32_t lds[];
-  uint32_t* h = lds;                     // [ntiles][E] tile histogram
-  uint32_t* gc = h + ntiles * E;         // [kMaskGroups][E] group counts -> group starts
-  uint32_t* tot = gc + kMaskGroups * E;  // [E] column totals
-  uint32_t* tpre = tot + E;              // [E] this tile's prefix per column
-  __shared__ uint32_t wsum[NT / kWave + 1];
+__global__ __launch_bounds__(kMaskSplitThreads) void mask_compact_kernel(const uint8_t* __restrict__ map,
+                                                                         const P* __restrict__ probs, int64_t T,
+                                                                         int32_t E, int ntiles,
+                                                                         const uint32_t* __restrict__ hist,
+                                                                         const uint32_t* __restrict__ range_tot,
+                                                                         P* __restrict__ pp, int64_t N) {
+  constexpr int NT = kMaskSplitThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int MC = kMaskRangeUnits * W;  // columns of a full range
+  constexpr int kHistBatch = 16;           // histogram words per thread per load round
+  constexpr int kRangeBatch = 4;           // range totals per thread per load round
+  __shared__ uint32_t gc[kMaskGroups * MC];  // [group][column] item counts -> offsets in the tile's column run
+  __shared__ uint32_t part[2 * NT];          // column partials: all tiles | earlier tiles
+  __shared__ uint32_t rsum[2 * NW];          // per-wave range totals: all | lower ranges
+  __shared__ uint32_t cst[MC], coff[MC];    // per column: output start, staging offset
+  __shared__ uint32_t staged;                // entries of the workgroup
+  __shared__ uint2 stage[kMaskRows * MC + kWave];  // (value, output position): column runs back to back; trash
   const int tid = threadIdx.x;
+  const int lane = static_cast<int>(lane_id());
   const int tile = blockIdx.x;
-  const int64_t t0 = static_cast<int64_t>(tile) * kMaskRows;
-  const int cu = E / W;
-  const int items = kMaskGroups * cu;
-  const int hw = ntiles * E;
-  // 1. every global load of the first round at once: the first histogram batch and this
-  //    thread's first item (map units and probs)
-  MaskItem<W, P> first;
-  const bool has_first = tid < items;
-  const int g0 = has_first ? tid / cu : 0;
-  const int c0 = has_first ? tid - g0 * cu : 0;
-  first.load(map, probs, T, E, t0 + g0 * kMaskGroupRows, c0);
-  for (int i0 = 0; i0 < hw; i0 += NT * 16) {
-    uint32_t v[16];
+  const int r = blockIdx.y;
+  const int R = gridDim.y;
+  const int u0 = r * kMaskRangeUnits;
+  const int nu = min(kMaskRangeUnits, E / W - u0);
+  const int ncols = nu * W;
+  const int e0 = u0 * W;
+  const int g = tid / kMaskRangeUnits, u = tid % kMaskRangeUnits;
+  const bool act = u < nu;
+  const int64_t r0 = static_cast<int64_t>(tile) * kMaskRows + g * kMaskGroupRows;
+  // 1. the global loads of the first round all at once: the item's map units and probs,
+  //    the thread's histogram words (column c, tiles q, q + ppc, ...), its range totals
+  MaskItem<W, P> item;
+  item.load(map, probs, T, E, r0, u0 + (act ? u : 0));
+  int ppc = 1;  // threads per column: a power of two, ppc * ncols <= NT
+  while (ppc * 2 * ncols <= NT) ppc *= 2;
+  const int c = tid % ncols, q = tid / ncols;
+  const int nrt = ntiles * R;
+  uint32_t call = 0, cpre = 0, rall = 0, rlow = 0;
+  for (int i = 0;; ++i) {
+    const int t0 = q + i * ppc * kHistBatch;
+    const int j0 = tid + i * NT * kRangeBatch;
+    const bool more_h = q < ppc && t0 < ntiles;
+    const bool more_r = j0 < nrt;
+    if (!(more_h || more_r)) break;
+    uint32_t hv[kHistBatch], rv[kRangeBatch];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = hist[min(i0 + u * NT + tid, hw - 1)];
+    for (int k = 0; k < kHistBatch; ++k)
+      hv[k] = hist[static_cast<int64_t>(min(t0 + k * ppc, ntiles - 1)) * E + e0 + c];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (i0 + u * NT + tid < hw) h[i0 + u * NT + tid] = v[u];
+    for (int k = 0; k < kRangeBatch; ++k) rv[k] = range_tot[min(j0 + k * NT, nrt - 1)];
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k) {
+      const int t = t0 + k * ppc;
+      call += (q < ppc && t < ntiles) ? hv[k] : 0u;
+      cpre += (q < ppc && t < tile) ? hv[k] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kRangeBatch; ++k) {
+      const int j = j0 + k * NT;
+      rall += j < nrt ? rv[k] : 0u;
+      rlow += (j < nrt && j % R < r) ? rv[k] : 0u;
+    }
   }
-  if (has_first) {
-    uint32_t cnt[W];
-    first.count(T, t0 + g0 * kMaskGroupRows, cnt);
+  uint32_t cnt[W];
+  item.count(T, r0, cnt);
+  if (act) {
 #pragma unroll
-    for (int w = 0; w < W; ++w) gc[g0 * E + c0 * W + w] = cnt[w];
+    for (int w = 0; w < W; ++w) gc[g * MC + u * W + w] = cnt[w];
   }
-  for (int it = tid + NT; it < items; it += NT) {  // wide maps: further items one by one
-    const int g = it / cu;
-    const int c = it - g * cu;
-    uint32_t x[kMaskGroupRows], cnt[W];
-    mask_item_counts<W>(map, T, E, t0 + g * kMaskGroupRows, c, x, cnt);
-#pragma unroll
-    for (int w = 0; w < W; ++w) gc[g * E + c * W + w] = cnt[w];
+  part[tid] = call;  // zero for q >= ppc
+  part[NT + tid] = cpre;
+  rall = wave_sum(rall);
+  rlow = wave_sum(rlow);
+  if (lane == 0) {
+    rsum[tid / kWave] = rall;
+    rsum[NW + tid / kWave] = rlow;
+  }
+  // 2. column sums: a tree over the ppc partials of each column
+  for (int h = ppc / 2; h >= 1; h /= 2) {
+    __syncthreads();
+    if (q < h) {
+      part[q * ncols + c] += part[(q + h) * ncols + c];
+      part[NT + q * ncols + c] += part[NT + (q + h) * ncols + c];
+    }
   }
   __syncthreads();
-  // 2. column totals and tile prefixes; thread i owns the columns [i*per, (i+1)*per)
-  const int per = (E + NT - 1) / NT;
-  const int lo = min(E, tid * per);
-  const int hi = min(E, lo + per);
-  uint32_t mine = 0;
-  for (int e = lo; e < hi; ++e) {
-    uint32_t t_all = 0, t_pre = 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const uint32_t v = h[t * E + e];
-      t_pre += (t < tile) ? v : 0u;
-      t_all += v;
-    }
-    tot[e] = t_all;
-    tpre[e] = t_pre;
-    mine += t_all;
+  uint32_t filled = 0, low = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    filled += rsum[w];
+    low += rsum[NW + w];
   }
-  uint32_t filled;
-  uint32_t start = block_exscan<NT>(mine, wsum, filled);  // first position of column lo
-  // 3. start of each row group of this tile, per column
-  for (int e = lo; e < hi; ++e) {
-    uint32_t run = start + tpre[e];
-    for (int g = 0; g < kMaskGroups; ++g) {
-      const uint32_t c = gc[g * E + e];
-      gc[g * E + e] = run;
-      run += c;
+  // 3. wave 0, one lane per column: the column's output start and, over the row groups,
+  //    each item's offset in the column's run; the runs are staged back to back
+  if (tid < kWave) {
+    const uint32_t tot = tid < ncols ? part[tid] : 0u;
+    uint32_t n = 0;
+    if (tid < ncols) {
+      for (int gg = 0; gg < kMaskGroups; ++gg) {
+        const uint32_t v = gc[gg * MC + tid];
+        gc[gg * MC + tid] = n;
+        n += v;
+      }
     }
-    start += tot[e];
+    const uint32_t incl_tot = wave_inclusive_scan(tot, lane);
+    const uint32_t incl_n = wave_inclusive_scan(n, lane);
+    if (tid < ncols) {
+      cst[tid] = low + incl_tot - tot + part[NT + tid];
+      coff[tid] = incl_n - n;
+    }
+    if (tid == kWave - 1) staged = incl_n;
   }
   __syncthreads();
-  // 4. place the tile's entries, rows in order within each item
-  if (has_first) {
-    uint32_t pos[W];
+  // 4. stage the item's entries, rows in order, then copy the staged entries out: the
+  //    column runs are consecutive positions, so neighbouring lanes store neighbours
+  if (act) {
+    uint32_t sp[W], gp[W];
 #pragma unroll
-    for (int w = 0; w < W; ++w) pos[w] = gc[g0 * E + c0 * W + w];
-    first.place(T, t0 + g0 * kMaskGroupRows, pos, pp, N);
+    for (int w = 0; w < W; ++w) {
+      const uint32_t o = gc[g * MC + u * W + w];
+      sp[w] = coff[u * W + w] + o;
+      gp[w] = cst[u * W + w] + o;
+    }
+    item.stage(T, r0, sp, gp, stage, kMaskRows * MC + lane);
   }
-  for (int it = tid + NT; it < items; it += NT) {
-    const int g = it / cu;
-    const int c = it - g * cu;
-    MaskItem<W, P> item;
-    item.load(map, probs, T, E, t0 + g * kMaskGroupRows, c);
-    uint32_t pos[W];
+  __syncthreads();
+  constexpr int kOut = 4;  // staged entries per thread per round, read together
+  const uint32_t M = staged;
+  for (uint32_t f0 = tid; f0 < M; f0 += kOut * NT) {
+    uint2 e[kOut];
 #pragma unroll
-    for (int w = 0; w < W; ++w) pos[w] = gc[g * E + c * W + w];
-    item.place(T, t0 + g * kMaskGroupRows, pos, pp, N);
+    for (int k = 0; k < kOut; ++k) e[k] = stage[min(f0 + k * NT, M - 1)];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k)
+      if (f0 + k * NT < M && e[k].y < N) pp[e[k].y] = static_cast<P>(e[k].x);
   }
   // 5. positions from the number of non-zero entries up to N get 0
-  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * NT + tid; gi < N; gi += static_cast<int64_t>(gridDim.x) * NT)
+  const int64_t nwg = static_cast<int64_t>(ntiles) * R;
+  const int64_t b = static_cast<int64_t>(tile) * R + r;
+  for (int64_t gi = b * NT + tid; gi < N; gi += nwg * NT)
     if (gi >= filled) pp[gi] = P(0);
+}
+
+// Words of the compaction's second workspace region: the column starts of the
+// three-launch path, or the range totals of the two-launch path (at most
+// tiles * mask_ranges(E, 1) of them, W = 1 giving the most ranges).
+static size_t mask_aux_words(int64_t E, int nt) {
+  const size_t ranges = static_cast<size_t>(mask_ranges(static_cast<int32_t>(E), 1));
+  return std::max(static_cast<size_t>(E) + 1, ranges * static_cast<size_t>(nt));
 }
 
 // Padded inversion, single pass: out_index / permute_token_id at the sorted position, and
@@ -511,7 +565,7 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
       p->mask_tiles = p->mask_fused ? fused_tiles : (p->T + kMaskTile - 1) / kMaskTile;
       const int nt = static_cast<int>(p->mask_tiles);
       c.take<uint32_t>(static_cast<size_t>(p->E) * nt);                 // histogram
-      c.take<uint32_t>(static_cast<size_t>(p->E) + 1);                  // column starts (three-launch path)
+      c.take<uint32_t>(mask_aux_words(p->E, nt));                        // column starts or range totals
       if (d->permute_probs == nullptr) c.take<uint8_t>(static_cast<size_t>(p->N) * p->pelt);
     }
     p->need_aux = d->out_index != nullptr || d->permute_token_id != nullptr;
@@ -628,7 +682,7 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     uint32_t* cstart = nullptr;
     if (p.has_probs) {
       mhist = c.take<uint32_t>(static_cast<size_t>(p.E) * nt);
-      cstart = c.take<uint32_t>(static_cast<size_t>(p.E) + 1);
+      cstart = c.take<uint32_t>(mask_aux_words(p.E, nt));  // three-launch path: column starts; else range totals
       if (pprobs == nullptr) pprobs = c.take<uint8_t>(static_cast<size_t>(p.N) * p.pelt);
     }
     SortBufs b{};
@@ -667,15 +721,14 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
       const uintptr_t pa = reinterpret_cast<uintptr_t>(d->probs);
       const bool wide = p.E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0 && pa % (4 * p.pelt) == 0;
       const int32_t E = static_cast<int32_t>(p.E);
-      const size_t count_lds = static_cast<size_t>(p.E) * sizeof(uint32_t);
-      const size_t lds = mask_compact_lds_words(nt, E) * sizeof(uint32_t);
       auto go = [&](auto wtag, auto ptag) {
         constexpr int W = decltype(wtag)::value;
         using P = decltype(ptag);
-        allow_large_lds(reinterpret_cast<const void*>(&mask_compact_kernel<W, P>), lds);
-        hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt), dim3(256), count_lds, s, map, p.T, E, mhist);
-        hipLaunchKernelGGL((mask_compact_kernel<W, P>), dim3(nt), dim3(kMaskCompactThreads), lds, s, map,
-                           static_cast<const P*>(d->probs), p.T, E, nt, mhist, static_cast<P*>(pprobs), p.N);
+        const dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(mask_ranges(E, W)));
+        hipLaunchKernelGGL(mask_tile_count_kernel<W>, grid, dim3(kMaskSplitThreads), 0, s, map, p.T, E, mhist,
+                           cstart);
+        hipLaunchKernelGGL((mask_compact_kernel<W, P>), grid, dim3(kMaskSplitThreads), 0, s, map,
+                           static_cast<const P*>(d->probs), p.T, E, nt, mhist, cstart, static_cast<P*>(pprobs), p.N);
       };
       if (wide) {
         if (p.pelt == 4) go(std::integral_constant<int, 4>(), uint32_t());
