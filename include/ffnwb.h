@@ -126,8 +126,11 @@ typedef struct ffnwb_batching_desc {
   int32_t* err_count;            /* [1] or NULL: number of unmasked slots whose expert or layer
                                     id was out of range (such slots are dropped) */
 
-  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
-     the row-gather kernel.  NULL = not recorded. */
+  /* Optional timing hooks (hipEvent_t), bound to the launch of the row-gather kernel: `begin`
+     takes the kernel's start and `end` its completion, from the kernel's own dispatch on
+     `stream`, so the span is the kernel alone and no event packet of its own is added to
+     the stream.  With only one of them given it is recorded on `stream` instead, before
+     or after the kernel.  NULL = not recorded. */
   void* ev_gather_begin;
   void* ev_gather_end;
 } ffnwb_batching_desc;
@@ -262,8 +265,11 @@ typedef struct moe_unpermute_desc {
   int32_t* permute_token_id;/* [N] */
   void* permute_probs;      /* [N] of probs_dtype (only with probs) */
 
-  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
-     the gather-reduce kernel.  NULL = not recorded. */
+  /* Optional timing hooks (hipEvent_t), bound to the launch of the gather-reduce kernel: `begin`
+     takes the kernel's start and `end` its completion, from the kernel's own dispatch on
+     `stream`, so the span is the kernel alone and no event packet of its own is added to
+     the stream.  With only one of them given it is recorded on `stream` instead, before
+     or after the kernel.  NULL = not recorded. */
   void* ev_reduce_begin;
   void* ev_reduce_end;
 
@@ -325,8 +331,11 @@ typedef struct moe_permute_desc {
   void* permuted_tokens;        /* [N, H] of dtype, dense */
   int32_t* sorted_indices;      /* [N] */
 
-  /* Optional timing hooks: hipEvent_t recorded on `stream` immediately before and after
-     the row-copy kernel.  NULL = not recorded. */
+  /* Optional timing hooks (hipEvent_t), bound to the launch of the row-copy kernel: `begin`
+     takes the kernel's start and `end` its completion, from the kernel's own dispatch on
+     `stream`, so the span is the kernel alone and no event packet of its own is added to
+     the stream.  With only one of them given it is recorded on `stream` instead, before
+     or after the kernel.  NULL = not recorded. */
   void* ev_copy_begin;
   void* ev_copy_end;
 } moe_permute_desc;

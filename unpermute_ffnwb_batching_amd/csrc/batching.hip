@@ -686,12 +686,13 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
 
   if (p.small) {
     const size_t lds = rank_lds_bytes(nb) + (static_cast<size_t>(nb) + 1 + 1024) * sizeof(uint32_t);
-    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
+    bool launched = false;
     err = launch_vec(p.vec, [&](auto v) {
-      hipLaunchKernelGGL(batching_small_kernel<decltype(v)::value>, dim3(1), dim3(kRankThreads), lds, s, a,
-                         p.pass.nbits, nb, d->group_list, d->expert_num, d->actual_token_num, d->err_count);
+      launched = launch_bound(batching_small_kernel<decltype(v)::value>, dim3(1), dim3(kRankThreads), lds, s,
+                              d->ev_gather_begin, d->ev_gather_end, a, p.pass.nbits, nb, d->group_list,
+                              d->expert_num, d->actual_token_num, d->err_count);
     });
-    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    if (!launched) return FFNWB_ERR_RUNTIME;
     return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
   }
 
@@ -721,13 +722,14 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
       default: go(std::integral_constant<int, 8>()); break;
     }
     if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
-    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
     const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+    bool launched = false;
     err = launch_vec(p.vec, [&](auto v) {
-      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of,
-                         first_of);
+      launched = launch_bound(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s,
+                              d->ev_gather_begin, d->ev_gather_end, a, static_cast<const uint32_t*>(pos_of),
+                              static_cast<const uint32_t*>(first_of));
     });
-    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    if (!launched) return FFNWB_ERR_RUNTIME;
     return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
   }
   if (p.range_order) {
@@ -738,13 +740,14 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
     hipLaunchKernelGGL(batching_order_kernel, dim3(rp.grid), dim3(kRoThreads), lds, s, a, static_cast<uint32_t>(nb),
                        rp.kr, rp.nbits, pos_of, d->group_list, d->expert_num, d->actual_token_num, d->err_count);
     if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
-    if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
     const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+    bool launched = false;
     err = launch_vec(p.vec, [&](auto v) {
-      hipLaunchKernelGGL(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pos_of,
-                         static_cast<const uint32_t*>(nullptr));
+      launched = launch_bound(batching_copy_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s,
+                              d->ev_gather_begin, d->ev_gather_end, a, static_cast<const uint32_t*>(pos_of),
+                              static_cast<const uint32_t*>(nullptr));
     });
-    if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+    if (!launched) return FFNWB_ERR_RUNTIME;
     return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
   }
   uint32_t* packed = c.take<uint32_t>(p.Y);
@@ -772,12 +775,13 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   const Placement pl{packed, hist, kstart, nb, p.pass.tile_shift};
-  if (!record_event(d->ev_gather_begin, s)) return FFNWB_ERR_RUNTIME;
   const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+  bool launched = false;
   err = launch_vec(p.vec, [&](auto v) {
-    hipLaunchKernelGGL(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s, a, pl);
+    launched = launch_bound(batching_gather_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s,
+                            d->ev_gather_begin, d->ev_gather_end, a, pl);
   });
-  if (!record_event(d->ev_gather_end, s)) return FFNWB_ERR_RUNTIME;
+  if (!launched) return FFNWB_ERR_RUNTIME;
   return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }
 

@@ -1,6 +1,7 @@
 // Host-side plans and launchers shared by the API layer and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -134,6 +135,42 @@ bool log_enabled();
 // Records an optional timing event (a hipEvent_t passed as void*) on stream s.
 inline bool record_event(void* ev, hipStream_t s) {
   return ev == nullptr || hipEventRecord(static_cast<hipEvent_t>(ev), s) == hipSuccess;
+}
+
+// Whether work enqueued on s is being captured into a graph (then events must be
+// recorded: a captured launch keeps no events bound to it).
+inline bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
+// Launches `kernel` on s with optional events bound to this launch: `begin` takes the
+// kernel's start and `end` its completion, from the kernel's own dispatch.  A bound event
+// puts no packet of its own on the stream (a recorded timing event costs several
+// microseconds of stream time and its span includes them).  Under graph capture, or
+// with only one event given, the events are recorded around the launch instead.
+// Returns false when the launch or a record fails.
+template <typename K, typename... Args>
+inline bool launch_bound(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, void* begin, void* end,
+                         Args... args) {
+  if ((begin != nullptr || end != nullptr) && stream_capturing(s)) {
+    if (!record_event(begin, s)) return false;
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    if (hipGetLastError() != hipSuccess) return false;
+    return record_event(end, s);
+  }
+  if (begin != nullptr && end != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<hipEvent_t>(begin), static_cast<hipEvent_t>(end), 0,
+                          args...);
+  } else {
+    if (!record_event(begin, s)) return false;
+    if (end != nullptr) {
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, s, nullptr, static_cast<hipEvent_t>(end), 0, args...);
+    } else {
+      hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    }
+  }
+  return hipGetLastError() == hipSuccess;
 }
 void log_warn(const char* fmt, ...);
 

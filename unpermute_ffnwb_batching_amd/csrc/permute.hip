@@ -475,30 +475,36 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   const unsigned blocks = static_cast<unsigned>((p.N + 3) / 4);
   const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
   uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
-  if (!record_event(d->ev_copy_begin, s)) return FFNWB_ERR_RUNTIME;
+  // the optional hooks are bound to the row-copy launch
+  void* evb = d->ev_copy_begin;
+  void* eve = d->ev_copy_end;
+  bool ok;
   if (!p.padded) {
     const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
     const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
     const int32_t K = static_cast<int32_t>(p.K);
+    const int32_t* sorted = d->sorted_indices;
+    const int32_t* src = source_of;
     if (vec == 16)
-      hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
-                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
+      ok = launch_bound(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
     else if (vec == 4)
-      hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
-                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
+      ok = launch_bound(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
     else
-      hipLaunchKernelGGL(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, tok, p.stride, p.row_bytes,
-                         d->sorted_indices, p.T, K, source_of, p.N, tb, out);
-  } else if (vec == 16)
-    hipLaunchKernelGGL(permute_rows_kernel<16>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
-                       p.N, out);
-  else if (vec == 4)
-    hipLaunchKernelGGL(permute_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
-                       p.N, out);
-  else
-    hipLaunchKernelGGL(permute_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, tok, p.stride, p.row_bytes, source_of,
-                       p.N, out);
-  if (!record_event(d->ev_copy_end, s)) return FFNWB_ERR_RUNTIME;
+      ok = launch_bound(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
+  } else if (vec == 16) {
+    ok = launch_bound(permute_rows_kernel<16>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
+                      static_cast<const int32_t*>(source_of), p.N, out);
+  } else if (vec == 4) {
+    ok = launch_bound(permute_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
+                      static_cast<const int32_t*>(source_of), p.N, out);
+  } else {
+    ok = launch_bound(permute_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
+                      static_cast<const int32_t*>(source_of), p.N, out);
+  }
+  if (!ok) return FFNWB_ERR_RUNTIME;
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }
 

@@ -627,35 +627,39 @@ static ReduceShape reduce_shape(bool vec, int64_t H, int elt) {
   return r;
 }
 
+// The optional hooks ev_begin / ev_end are bound to the reduce launch; with no launch
+// (T = 0) they are recorded back to back.
 template <class TT, class TW, int MODE>
-static void launch_reduce_t(const ReduceArgs& ra, const ReduceShape& sh, int64_t T, hipStream_t s) {
-  if (T == 0) return;
+static bool launch_reduce_t(const ReduceArgs& ra, const ReduceShape& sh, int64_t T, hipStream_t s, void* evb,
+                            void* eve) {
+  if (T == 0) return record_event(evb, s) && record_event(eve, s);
   const dim3 grid(static_cast<unsigned>(T)), block(sh.threads);
   switch (sh.cpt) {
-    case 0: hipLaunchKernelGGL((unpermute_reduce_elem_kernel<TT, TW, MODE>), grid, block, 0, s, ra); break;
-    case 1: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 1>), grid, block, 0, s, ra); break;
-    case 2: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 2>), grid, block, 0, s, ra); break;
-    default: hipLaunchKernelGGL((unpermute_reduce_kernel<TT, TW, MODE, 4>), grid, block, 0, s, ra); break;
+    case 0: return launch_bound(unpermute_reduce_elem_kernel<TT, TW, MODE>, grid, block, 0, s, evb, eve, ra);
+    case 1: return launch_bound(unpermute_reduce_kernel<TT, TW, MODE, 1>, grid, block, 0, s, evb, eve, ra);
+    case 2: return launch_bound(unpermute_reduce_kernel<TT, TW, MODE, 2>, grid, block, 0, s, evb, eve, ra);
+    default: return launch_bound(unpermute_reduce_kernel<TT, TW, MODE, 4>, grid, block, 0, s, evb, eve, ra);
   }
 }
 
 template <class TT, class TW>
-static void launch_reduce_w(const ReduceArgs& ra, int mode, const ReduceShape& sh, int64_t T, hipStream_t s) {
+static bool launch_reduce_w(const ReduceArgs& ra, int mode, const ReduceShape& sh, int64_t T, hipStream_t s,
+                            void* evb, void* eve) {
   switch (mode) {
-    case kNonPad: launch_reduce_t<TT, TW, kNonPad>(ra, sh, T, s); break;
-    case kNonPadW2: launch_reduce_t<TT, TW, kNonPadW2>(ra, sh, T, s); break;
-    case kNonPadW1: launch_reduce_t<TT, TW, kNonPadW1>(ra, sh, T, s); break;
-    case kPad: launch_reduce_t<TT, TW, kPad>(ra, sh, T, s); break;
-    default: launch_reduce_t<TT, TW, kPadW>(ra, sh, T, s); break;
+    case kNonPad: return launch_reduce_t<TT, TW, kNonPad>(ra, sh, T, s, evb, eve);
+    case kNonPadW2: return launch_reduce_t<TT, TW, kNonPadW2>(ra, sh, T, s, evb, eve);
+    case kNonPadW1: return launch_reduce_t<TT, TW, kNonPadW1>(ra, sh, T, s, evb, eve);
+    case kPad: return launch_reduce_t<TT, TW, kPad>(ra, sh, T, s, evb, eve);
+    default: return launch_reduce_t<TT, TW, kPadW>(ra, sh, T, s, evb, eve);
   }
 }
 
-static void launch_reduce(const ReduceArgs& ra, int dtype, int pdtype, int mode, const ReduceShape& sh, int64_t T,
-                          hipStream_t s) {
-  if (dtype == FFNWB_DT_FP16) launch_reduce_w<TF16, TF16>(ra, mode, sh, T, s);
-  else if (dtype == FFNWB_DT_FP32) launch_reduce_w<TF32, TF32>(ra, mode, sh, T, s);
-  else if (pdtype == FFNWB_DT_FP32) launch_reduce_w<TBF16, TF32>(ra, mode, sh, T, s);
-  else launch_reduce_w<TBF16, TBF16>(ra, mode, sh, T, s);
+static bool launch_reduce(const ReduceArgs& ra, int dtype, int pdtype, int mode, const ReduceShape& sh, int64_t T,
+                          hipStream_t s, void* evb, void* eve) {
+  if (dtype == FFNWB_DT_FP16) return launch_reduce_w<TF16, TF16>(ra, mode, sh, T, s, evb, eve);
+  if (dtype == FFNWB_DT_FP32) return launch_reduce_w<TF32, TF32>(ra, mode, sh, T, s, evb, eve);
+  if (pdtype == FFNWB_DT_FP32) return launch_reduce_w<TBF16, TF32>(ra, mode, sh, T, s, evb, eve);
+  return launch_reduce_w<TBF16, TBF16>(ra, mode, sh, T, s, evb, eve);
 }
 
 int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* ws, hipStream_t s) {
@@ -688,17 +692,43 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     SortBufs b{};
     const bool aux = p.need_aux && p.N > 0;
     if (aux) carve_sort_bufs(c, p.sort, p.N, &b);
-    // auxiliary order (out_index / permute_token_id) on the side stream
+    // The auxiliary order (out_index / permute_token_id) runs on the side stream.  The
+    // lock covers the fork, the side stream's work and the caller stream's wait for the
+    // join, so that no other call re-records the shared events in between.
+    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
     SideStream* side = nullptr;
     if (aux) {
-      std::lock_guard<std::mutex> lock(g_side_mu);
+      lock.lock();
       side = side_stream_for(s);
+    }
+    const bool fused = p.has_probs && nt > 0 && p.mask_fused;
+    const uint8_t* map = d->routing_map;
+    const int32_t E = static_cast<int32_t>(p.E);
+    const bool wide = fused && p.E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0 &&
+                      reinterpret_cast<uintptr_t>(d->probs) % (4 * p.pelt) == 0;
+    // 1. the first kernel on the caller's stream: the compaction's count kernel, whose
+    //    completion (all earlier work on the stream done) is the fork point; without it a
+    //    fork event is recorded
+    bool forked = false;
+    if (fused) {
+      void* fork_ev = side != nullptr ? static_cast<void*>(side->fork) : nullptr;
+      const int W = wide ? 4 : 1;
+      const dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(mask_ranges(E, W)));
+      const bool ok = wide ? launch_bound(mask_tile_count_kernel<4>, grid, dim3(kMaskSplitThreads), 0, s, nullptr,
+                                          fork_ev, map, p.T, E, mhist, cstart)
+                           : launch_bound(mask_tile_count_kernel<1>, grid, dim3(kMaskSplitThreads), 0, s, nullptr,
+                                          fork_ev, map, p.T, E, mhist, cstart);
+      if (!ok) return FFNWB_ERR_RUNTIME;
+      forked = fork_ev != nullptr;
+    } else if (side != nullptr) {
+      forked = hipEventRecord(side->fork, s) == hipSuccess;
+    }
+    if (aux) {
       hipStream_t as = s;
-      if (side != nullptr && hipEventRecord(side->fork, s) == hipSuccess &&
-          hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess) {
+      if (side != nullptr && forked && hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess) {
         as = side->stream;
       } else {
-        side = nullptr;
+        side = nullptr;  // the order runs on the caller's stream
       }
       KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
       const uint32_t *kin, *vin;
@@ -715,18 +745,12 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
                            d->permute_token_id, sI, static_cast<int32_t>(p.K));
       if (side != nullptr && hipEventRecord(side->join, side->stream) != hipSuccess) return FFNWB_ERR_RUNTIME;
     }
-    // probs compaction, then the gather-reduce, on the caller's stream
-    if (p.has_probs && nt > 0 && p.mask_fused) {
-      const uint8_t* map = d->routing_map;
-      const uintptr_t pa = reinterpret_cast<uintptr_t>(d->probs);
-      const bool wide = p.E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0 && pa % (4 * p.pelt) == 0;
-      const int32_t E = static_cast<int32_t>(p.E);
+    // 2. the rest of the probs compaction, then the gather-reduce, on the caller's stream
+    if (fused) {
       auto go = [&](auto wtag, auto ptag) {
         constexpr int W = decltype(wtag)::value;
         using P = decltype(ptag);
         const dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(mask_ranges(E, W)));
-        hipLaunchKernelGGL(mask_tile_count_kernel<W>, grid, dim3(kMaskSplitThreads), 0, s, map, p.T, E, mhist,
-                           cstart);
         hipLaunchKernelGGL((mask_compact_kernel<W, P>), grid, dim3(kMaskSplitThreads), 0, s, map,
                            static_cast<const P*>(d->probs), p.T, E, nt, mhist, cstart, static_cast<P*>(pprobs), p.N);
       };
@@ -755,9 +779,8 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     ra.K = static_cast<int32_t>(p.K);
     ra.w = pprobs;
     const int mode = !p.has_probs ? kNonPad : (d->weight_index == 1 ? kNonPadW1 : kNonPadW2);
-    if (!record_event(d->ev_reduce_begin, s)) return FFNWB_ERR_RUNTIME;
-    launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s);
-    if (!record_event(d->ev_reduce_end, s)) return FFNWB_ERR_RUNTIME;
+    if (!launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s, d->ev_reduce_begin, d->ev_reduce_end))
+      return FFNWB_ERR_RUNTIME;
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
   } else {
     SortBufs b{};
@@ -818,9 +841,8 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     ra.order = order;
     ra.w = pprobs;
     const int mode = p.has_probs ? kPadW : kPad;
-    if (!record_event(d->ev_reduce_begin, s)) return FFNWB_ERR_RUNTIME;
-    launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s);
-    if (!record_event(d->ev_reduce_end, s)) return FFNWB_ERR_RUNTIME;
+    if (!launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s, d->ev_reduce_begin, d->ev_reduce_end))
+      return FFNWB_ERR_RUNTIME;
   }
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }
