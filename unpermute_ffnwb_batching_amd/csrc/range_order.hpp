@@ -109,19 +109,21 @@ __device__ __forceinline__ uint32_t* ro_counters(uint32_t* lds) { return lds + k
 // Pass 1 over this wave's slice.  Returns the lane's count of elements with key < lo;
 // `len` = the wave's number of owned elements (uniform).  seen(j, key, valid, err) is
 // called for every element of the slice (j < e).
-template <class KS, class Seen>
+// U blocks of loads are issued together (the default kRoUnroll, or a whole slice's
+// worth where registers allow).
+template <int U = kRoUnroll, class KS, class Seen>
 __device__ __forceinline__ uint32_t ro_count(const KS& ks, uint32_t b, uint32_t e, uint32_t lo, uint32_t kr,
                                              const RoWave& wv, uint32_t& len, Seen seen) {
   const uint32_t lane = lane_id();
   uint32_t below = 0;
   uint32_t n_own = 0;
-  for (uint32_t j0 = b; j0 < e; j0 += kRoUnroll * kRoBlock) {
-    uint32_t key[kRoUnroll][kRoVec];
-    bool v[kRoUnroll][kRoVec], er[kRoUnroll][kRoVec];
+  for (uint32_t j0 = b; j0 < e; j0 += U * kRoBlock) {
+    uint32_t key[U][kRoVec];
+    bool v[U][kRoVec], er[U][kRoVec];
 #pragma unroll
-    for (int u = 0; u < kRoUnroll; ++u) ks.key4(j0 + u * kRoBlock + lane * kRoVec, key[u], v[u], er[u]);
+    for (int u = 0; u < U; ++u) ks.key4(j0 + u * kRoBlock + lane * kRoVec, key[u], v[u], er[u]);
 #pragma unroll
-    for (int u = 0; u < kRoUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t jl = j0 + u * kRoBlock + lane * kRoVec;
       bool own[kRoVec];
 #pragma unroll

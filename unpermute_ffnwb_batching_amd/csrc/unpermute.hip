@@ -335,8 +335,8 @@ __global__ __launch_bounds__(256) void padded_scatter_kernel(const int32_t* __re
 // token (invalid ids share the last key T).  Workgroup b owns the keys [lo, lo + kr): it
 // writes seg[t], the first sorted position of token t, for its keys, and out_index /
 // permute_token_id at the sorted positions of its entries; the workgroup that owns key T
-// also writes seg[T + 1] = n.  Every workgroup gathers permute_probs for its share of the
-// entries first.
+// also writes seg[T + 1] = n.  Every workgroup also gathers permute_probs for its share of
+// the entries, its first ids loaded in the count pass's load round.
 template <typename P>
 __global__ __launch_bounds__(kRoThreads) void padded_order_kernel(const int32_t* __restrict__ sI, int32_t T,
                                                                   int64_t n, uint32_t kr, int nbits,
@@ -352,23 +352,27 @@ __global__ __launch_bounds__(kRoThreads) void padded_order_kernel(const int32_t*
   const uint32_t krr = min(kr, nkeys - lo);
   uint32_t* cnt = ro_counters(lds_words);
   for (int i = threadIdx.x; i < kRoWaves * static_cast<int>(krr); i += kRoThreads) cnt[i] = 0u;
-  if (pp != nullptr) {
-    const int64_t share = (n + gridDim.x - 1) / gridDim.x;
-    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * share;
-    const int64_t j1 = min(n, j0 + share);
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += kRoThreads) {
-      const int32_t v = sI[j];
-      pp[j] = (v >= 0 && v < T) ? probs[static_cast<int64_t>(v) * E + j / C] : P(0);
-    }
-  }
   __syncthreads();
+  // permute_probs for this workgroup's share of the entries: the first id is loaded with
+  // the count pass's keys and its prob after the pass, so the gather adds one load round
+  const int64_t share = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * share + threadIdx.x;
+  const int64_t j1 = min(n, static_cast<int64_t>(blockIdx.x) * share + share);
+  const int32_t v0 = sI[min(j0, n - 1)];
   const int w = uniform(static_cast<int>(threadIdx.x) / kWave);
   uint32_t b, e;
   ro_slice(static_cast<uint32_t>(n), w, b, e);
   const RoKeysPadded ks{sI, T, static_cast<uint32_t>(n)};
   const RoWave wv = ro_wave(lds_words, w, krr);
   uint32_t len;
-  const uint32_t below = ro_count(ks, b, e, lo, krr, wv, len, [](uint32_t, uint32_t, bool, bool) {});
+  // 8 blocks of loads at once: a whole 2048-entry slice in one round
+  const uint32_t below = ro_count<8>(ks, b, e, lo, krr, wv, len, [](uint32_t, uint32_t, bool, bool) {});
+  if (pp != nullptr) {
+    for (int64_t j = j0; j < j1; j += kRoThreads) {
+      const int32_t v = j == j0 ? v0 : sI[j];
+      pp[j] = (v >= 0 && v < T) ? probs[static_cast<int64_t>(v) * E + j / C] : P(0);
+    }
+  }
   uint32_t kcount, end;
   const uint32_t first = ro_middle(cnt, krr, below, wsum, kcount, end);
   if (threadIdx.x < krr) seg[lo + threadIdx.x] = first;
