@@ -28,6 +28,8 @@ HIPCC_FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # Keep hipcc from emitting packed-FP32 instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wextra",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -761,10 +761,10 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
                                                                : &sort_rank_kernel<16, KeyBatching>), lds);
   if (p.pass.R == 4)
     hipLaunchKernelGGL((sort_rank_kernel<4, KeyBatching>), dim3(p.pass.nt), dim3(kRankThreads), lds, s, ks, p.Y, 0,
-                       p.pass.nbits, nb, packed, hist, p.pass.nt, tile_err);
+                       p.pass.nbits, nb, packed, hist, tile_err);
   else
     hipLaunchKernelGGL((sort_rank_kernel<16, KeyBatching>), dim3(p.pass.nt), dim3(kRankThreads), lds, s, ks, p.Y, 0,
-                       p.pass.nbits, nb, packed, hist, p.pass.nt, tile_err);
+                       p.pass.nbits, nb, packed, hist, tile_err);
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   ScanTail tail{d->group_list, d->expert_num, d->actual_token_num, d->err_count, tile_err};

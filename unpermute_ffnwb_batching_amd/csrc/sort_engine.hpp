@@ -148,7 +148,7 @@ struct KeyArray {
 template <int R, class KS>
 __global__ __launch_bounds__(kRankThreads) void sort_rank_kernel(KS ks, int64_t n, int shift, int nbits, int nb,
                                                                  uint32_t* __restrict__ packed,
-                                                                 uint32_t* __restrict__ hist_g, int nt,
+                                                                 uint32_t* __restrict__ hist_g,
                                                                  uint32_t* __restrict__ tile_err) {
   extern __shared__ uint32_t lds_words[];
   __shared__ uint32_t err_w[kRankWaves];
@@ -242,7 +242,7 @@ __device__ __forceinline__ uint32_t walk_column(uint32_t* __restrict__ h, int nb
   return run;
 }
 
-static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t* __restrict__ h, int nb, int nt,
+[[maybe_unused]] static __global__ __launch_bounds__(kScanThreads) void scan_hist_kernel(uint32_t* __restrict__ h, int nb, int nt,
                                                                         uint32_t* __restrict__ start,
                                                                         uint32_t* __restrict__ total_out,
                                                                         ScanTail tail) {
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void lsd_scatter_kernel(KS ks, const uint32_t*
 
 // seg[k] = first sorted position whose key is >= k, for k in [0, nkeys]; seg[nkeys] = n
 // when every key is < nkeys.  Each seg entry is written by exactly one thread.
-static __global__ __launch_bounds__(256) void segment_bounds_kernel(const uint32_t* __restrict__ skeys, int64_t n,
+[[maybe_unused]] static __global__ __launch_bounds__(256) void segment_bounds_kernel(const uint32_t* __restrict__ skeys, int64_t n,
                                                              uint32_t nkeys, uint32_t* __restrict__ seg) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j > n) return;

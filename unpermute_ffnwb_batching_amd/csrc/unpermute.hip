@@ -411,10 +411,10 @@ static void launch_rank(const SortPass& p, KS ks, uint32_t* packed, uint32_t* hi
   allow_large_lds(reinterpret_cast<const void*>(p.R == 4 ? &sort_rank_kernel<4, KS> : &sort_rank_kernel<16, KS>), lds);
   if (p.R == 4)
     hipLaunchKernelGGL((sort_rank_kernel<4, KS>), dim3(p.nt), dim3(kRankThreads), lds, s, ks, p.n, p.shift, p.nbits,
-                       p.nb, packed, hist, p.nt, tile_err);
+                       p.nb, packed, hist, tile_err);
   else
     hipLaunchKernelGGL((sort_rank_kernel<16, KS>), dim3(p.nt), dim3(kRankThreads), lds, s, ks, p.n, p.shift,
-                       p.nbits, p.nb, packed, hist, p.nt, tile_err);
+                       p.nbits, p.nb, packed, hist, tile_err);
 }
 
 // Scans a histogram of nb digits x nt tiles and returns where its elements go.
