@@ -16,8 +16,8 @@ Also reported, per workload: the median, p10 and p90 call time with L2 and the
 Infinity Cache flushed (a 1 GiB write) before every iteration, the warm back-to-back
 time, and a plain device copy moving the same number of bytes (what a streaming kernel
 reaches); the roofline of the dominant kernel (the non-padded gather-reduce, timed with
-HIP events on its own stream position); and the CPU oracle timed on the host (median of
-3 runs per workload).
+HIP events bound to its launch, so the span is that kernel alone); and the CPU oracle
+timed on the host (median of 3 runs per workload).
 """
 
 import argparse
@@ -427,7 +427,7 @@ def main():
     K, W = args.steps, args.warmup
     have_np = "unpermute_nonpadded" in calls
     from unpermute_ffnwb_batching_amd.hip_events import HipEvent
-    # fence-free HIP events, recorded by the library around the gather-reduce kernel
+    # fence-free HIP events, bound by the library to the gather-reduce kernel's launch
     hot = [(HipEvent(), HipEvent()) for _ in range(K)]
 
     def step(i=None):

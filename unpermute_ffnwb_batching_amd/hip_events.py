@@ -1,8 +1,9 @@
 """Minimal HIP timing events for the library's timing hooks (plumbing only).
 
-The descriptors' ev_* fields take hipEvent_t handles.  These events are created with
-hipEventDisableSystemFence: recording them does not issue a system-scope release, so
-timing a kernel inside a sequence of launches does not stall the stream.
+The descriptors' ev_* fields take hipEvent_t handles, which the library binds to the
+timed kernel's launch (or records on the stream under graph capture).  These events are
+created with hipEventDisableSystemFence: completing them issues no system-scope release,
+so timing a kernel inside a sequence of launches does not stall the stream.
 """
 
 import ctypes
