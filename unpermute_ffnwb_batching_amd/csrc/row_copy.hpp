@@ -34,6 +34,16 @@ struct RowPiece {
       if (i < n16) __builtin_nontemporal_store(v[u], d4 + i);
     }
   }
+  // the same with ordinary stores
+  __device__ __forceinline__ void store_cached(uint8_t* __restrict__ dst, int64_t n16, int64_t b,
+                                               uint32_t lane) const {
+    V* d4 = reinterpret_cast<V*>(dst);
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) d4[i] = v[u];
+    }
+  }
 };
 
 // Copies bytes [from, bytes) of a row (the part not moved by an earlier piece).
