@@ -129,8 +129,9 @@ typedef struct ffnwb_batching_desc {
   /* Optional timing hooks (hipEvent_t), bound to the launch of the row-gather kernel: `begin`
      takes the kernel's start and `end` its completion, from the kernel's own dispatch on
      `stream`, so the span is the kernel alone and no event packet of its own is added to
-     the stream.  With only one of them given it is recorded on `stream` instead, before
-     or after the kernel.  NULL = not recorded. */
+     the stream.  A lone `begin` is recorded on `stream` before the kernel instead (a lone
+     `end` is still bound), and under graph capture both are recorded around it.
+     NULL = not recorded. */
   void* ev_gather_begin;
   void* ev_gather_end;
 } ffnwb_batching_desc;
@@ -268,8 +269,9 @@ typedef struct moe_unpermute_desc {
   /* Optional timing hooks (hipEvent_t), bound to the launch of the gather-reduce kernel: `begin`
      takes the kernel's start and `end` its completion, from the kernel's own dispatch on
      `stream`, so the span is the kernel alone and no event packet of its own is added to
-     the stream.  With only one of them given it is recorded on `stream` instead, before
-     or after the kernel.  NULL = not recorded. */
+     the stream.  A lone `begin` is recorded on `stream` before the kernel instead (a lone
+     `end` is still bound), and under graph capture both are recorded around it.
+     NULL = not recorded. */
   void* ev_reduce_begin;
   void* ev_reduce_end;
 
@@ -334,8 +336,9 @@ typedef struct moe_permute_desc {
   /* Optional timing hooks (hipEvent_t), bound to the launch of the row-copy kernel: `begin`
      takes the kernel's start and `end` its completion, from the kernel's own dispatch on
      `stream`, so the span is the kernel alone and no event packet of its own is added to
-     the stream.  With only one of them given it is recorded on `stream` instead, before
-     or after the kernel.  NULL = not recorded. */
+     the stream.  A lone `begin` is recorded on `stream` before the kernel instead (a lone
+     `end` is still bound), and under graph capture both are recorded around it.
+     NULL = not recorded. */
   void* ev_copy_begin;
   void* ev_copy_end;
 } moe_permute_desc;

@@ -1,9 +1,9 @@
 """Timing hooks bound to the timed kernel's launch.
 
-Every entry point that takes hooks runs with both hooks given (bound to the kernel's
-dispatch) and with only the end hook (recorded on the stream after the kernel).  Its
-results still match the oracle, and the bound span is positive, finite and shorter
-than the whole call measured on the host around a synchronisation.
+Every entry point that takes hooks runs with both hooks given and with only the end
+hook (both bound to the kernel's dispatch).  Its results still match the oracle, and the
+bound span is positive, finite and shorter than the whole call measured on the host
+around a synchronisation.
 """
 
 import time

@@ -147,9 +147,9 @@ inline bool stream_capturing(hipStream_t s) {
 // Launches `kernel` on s with optional events bound to this launch: `begin` takes the
 // kernel's start and `end` its completion, from the kernel's own dispatch.  A bound event
 // puts no packet of its own on the stream (a recorded timing event costs several
-// microseconds of stream time and its span includes them).  Under graph capture, or
-// with only one event given, the events are recorded around the launch instead.
-// Returns false when the launch or a record fails.
+// microseconds of stream time and its span includes them).  A lone `begin` is recorded
+// on s before the launch (a lone `end` is still bound); under graph capture both are
+// recorded around the launch.  Returns false when the launch or a record fails.
 template <typename K, typename... Args>
 inline bool launch_bound(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, void* begin, void* end,
                          Args... args) {
