@@ -30,6 +30,8 @@ NONPAD = [
     (3000, 8, 64, 32, synth.BF16, synth.FP32, 2000, True, "compact"),  # aux order needs 2 LSD passes
     (40000, 8, 64, 16, synth.BF16, synth.FP32, 30000, True, "compact"),  # 320000 slots
     (20000, 4, 129, 16, synth.BF16, synth.FP32, 5000, True, "compact"),  # 79 tiles x 17 column ranges
+    (300, 4, 1100, 16, synth.BF16, synth.FP32, 100, True, "compact"),    # E > 1024: three-launch compaction
+    (70000, 2, 64, 8, synth.FP16, synth.FP16, 20000, True, "slots"),     # 274 tiles x 64 > 16384 words: the same
     (2, 512, 600, 16, synth.FP16, synth.FP16, 100, True, "slots"),    # topK = 512
     (1000, 2, 300, 264, synth.FP32, synth.FP32, 0, True, "compact"),
 ]
