@@ -2,12 +2,16 @@
 // "Function description and formulas", branches 1-4; "Kernel implementation").
 //
 // Non-padded mode (branches 2 and 4):
-//   [probs]  probs compaction: stable counting sort of the non-zero routing-map entries
-//            j = t*E + e by expert e (rank, scan, scatter) -> permute_probs, zero-padded;
+//   [probs]  probs compaction: the non-zero routing-map entries in expert-major order
+//            -> permute_probs, zero-padded.  Two launches over 256-token tiles split by
+//            column ranges (count, then compact), or for large maps a counting sort
+//            (count, scan, scatter);
 //   reduce:  one workgroup per token gathers its topK slots' permuted rows and sums
 //            x * w in FP32 (slot order), one RNE store;
 //   [aux]    out_index / permute_token_id: stable sort of the slots by sortedIndices+1
-//            (LSD passes when the row count exceeds one pass's bucket budget).
+//            (LSD passes when the row count exceeds one pass's bucket budget), on the
+//            library's side stream, forked when the compaction's first kernel completes
+//            and joined after the reduce.
 // Padded mode (branches 1 and 3):
 //   invert:  stable counting sort of the capacity entries by token id (rank, scan,
 //            scatter -> out_index, permute_token_id, permute_probs, per-token segments);
@@ -484,7 +488,8 @@ static Placement run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const S
 // A library-owned stream per device on which the non-padded auxiliary sort runs, forked
 // from and joined back to the caller's stream with events, so that it overlaps the probs
 // compaction and the gather-reduce (it depends only on sortedIndices).  Created on first
-// use at the default priority; the mutex keeps each fork's record/wait pair together.
+// use at the default priority; the mutex is held from a call's fork to its join wait,
+// so that no other call re-records the shared events in between.
 // Both streams live on one device, so the events skip the system-scope fence (a
 // device-scope release orders the side stream's writes for the caller's stream); with
 // the fence each record left the stream idle for several microseconds.
