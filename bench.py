@@ -146,9 +146,11 @@ def padded_bytes(c):
 
 
 def permute_bytes(c, ref_nnz):
-    """Forward permute: the map, each token row once, every output row, the indices."""
+    """Forward permute: the map, each token row once, every output row, the indices
+    (non-padded: N rows and slots; padded: the E*C capacity rows and entries)."""
     elt = {0: 2, 1: 2, 2: 1, 3: 4}[c["dtype"]]
-    return c["T"] * c["E"] + c["T"] * c["H"] * elt + c["N"] * c["H"] * elt + 4 * c["N"]
+    n_out = c["E"] * c["C"] if c.get("padded") else c["N"]
+    return c["T"] * c["E"] + c["T"] * c["H"] * elt + n_out * c["H"] * elt + 4 * n_out
 
 
 def padded_skip_bytes(c):
@@ -297,15 +299,15 @@ def measure_update_expert(args, stream):
     return res
 
 
-def measure_permute(args, stream):
-    """The forward permute (a widening of the path) at the non-padded workload's shape:
-    flushed-cache medians, the row-copy kernel's steady-state time from fence-free HIP
-    events, and (with the CPU leg) parity with the oracle."""
+def measure_permute(args, stream, padded=False):
+    """The forward permute (a widening of the path) at the non-padded (or padded)
+    unpermute workload's shape: flushed-cache medians, the row-copy kernel's steady-state
+    time from fence-free HIP events, and (with the CPU leg) parity with the oracle."""
     import torch
     import synth
     from _gpu import prepare_permute, fetch_permute
     from unpermute_ffnwb_batching_amd.hip_events import HipEvent
-    c = synth.permute_config()
+    c = synth.permute_padded_config() if padded else synth.permute_config()
     call = prepare_permute(c)
     for _ in range(3):
         call.run(stream)
@@ -323,7 +325,9 @@ def measure_permute(args, stream):
     call_ms = s0.elapsed_time(s1) / K
     copy_ms = float(np.mean([b.elapsed_ms(e) for b, e in ev]))
     call.set_copy_events(None, None)
-    res = {"shape": "T=16384 topK=8 E=128 H=4096 bf16, 8 uniform experts per token",
+    shape = ("E=64 C=512 T=8192 H=5120 fp16, 4 uniform experts per token" if padded
+             else "T=16384 topK=8 E=128 H=4096 bf16, 8 uniform experts per token")
+    res = {"shape": shape,
            "alg_bytes": alg, "us_per_call": round(call_ms * 1e3, 2), "GBps": round(alg / call_ms / 1e6, 1),
            "copy_kernel_us": round(copy_ms * 1e3, 2),
            "copy_kernel_GBps": round((alg - c["T"] * c["E"]) / copy_ms / 1e6, 1)}
@@ -533,6 +537,7 @@ def main():
         pass
     elif not args.only or "permute" in args.only.split(","):
         next_rows["moe_permute_nonpadded"] = measure_permute(args, stream)
+        next_rows["moe_permute_padded"] = measure_permute(args, stream, padded=True)
     if not args.no_next_rows and (not args.only or "context" in args.only.split(",")):
         next_rows["batching_from_context"] = measure_ctx(args, stream)
     if not args.no_next_rows and (not args.only or "update_expert" in args.only.split(",")):

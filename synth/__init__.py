@@ -305,6 +305,12 @@ def permute_config():
     return permute_case(6, T=16384, K=8, E=128, H=4096, dtype=BF16, n_t=np.full(16384, 8))
 
 
+def permute_padded_config():
+    """Padded forward permute at the padded unpermute workload's shape (E=64, C=512,
+    T=8192, H=5120 FP16): every token routed to 4 distinct uniform experts."""
+    return permute_case(7, T=8192, K=4, E=64, H=5120, dtype=FP16, padded=True, C=512, n_t=np.full(8192, 4))
+
+
 def config(n):
     return batching_config(n) if n <= 3 else unpermute_config(n)
 
