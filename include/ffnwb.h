@@ -32,8 +32,8 @@
  *     never allocates, frees or synchronises; it only enqueues kernels on
  *     `stream` (a hipStream_t; NULL = the legacy default stream) and returns.
  *   - The caller allocates the workspace (device memory of the size the query
- *     returned, 256-byte aligned) and keeps it alive until the work on `stream`
- *     has finished.  Its contents on entry do not matter.
+ *     returned, 256-byte aligned; FFNWB_ERR_WORKSPACE otherwise) and keeps it alive
+ *     until the work on `stream` has finished.  Its contents on entry do not matter.
  *   - Inputs are read-only.  Inputs and outputs must not overlap.
  *   - Calls are stateless and may run concurrently on different streams with
  *     distinct workspaces and outputs.
@@ -62,7 +62,7 @@ extern "C" {
 #define FFNWB_ERR_PARAM_NULLPTR  161001 /* a required pointer is NULL */
 #define FFNWB_ERR_PARAM_INVALID  161002 /* a type, shape or range is outside the supported set */
 #define FFNWB_ERR_INNER_NULLPTR  561103 /* unpermute: topK > 512, or probs has an unsupported shape */
-#define FFNWB_ERR_WORKSPACE      1      /* workspace NULL or smaller than the query returned */
+#define FFNWB_ERR_WORKSPACE      1      /* workspace NULL, smaller than the query returned, or not 256-byte aligned */
 #define FFNWB_ERR_RUNTIME        2      /* the HIP runtime refused a launch or a device query */
 
 /* Element types. 0..2 are the batching page's tokenDtype values. */
@@ -142,7 +142,8 @@ typedef struct ffnwb_batching_desc {
 int ffnwb_batching_workspace_size(const ffnwb_batching_desc* d, size_t* ws_bytes);
 
 /* Validates again, then enqueues the batching on `stream`.  `workspace` must hold at
-   least the queried size (FFNWB_ERR_WORKSPACE otherwise; NULL allowed when it is 0). */
+   least the queried size and be 256-byte aligned (FFNWB_ERR_WORKSPACE otherwise; NULL
+   allowed when the size is 0). */
 int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------

@@ -303,7 +303,27 @@ def test_permute_workspace():
     st, n = _pws(_permute_desc(num_tokens=16384, num_experts=128, num_out_rows=16384 * 8))
     assert st == 0 and n >= 4 * 16384 * 8            # source token of every row
     st, n = _pws(_permute_desc(padded_mode=1, num_tokens=8192, num_experts=64, num_out_rows=64 * 512, capacity=512))
-    assert st == 0 and n >= 4 * 32 * 64               # tile histogram only
+    assert st == 0 and n >= 4 * 32 * 64 + 4 * 8192 * 64  # tile histogram, capacity row of every entry
+
+
+def test_launch_rejects_misaligned_workspace_before_any_device_work():
+    """The workspace must be 256-byte aligned (the kernels store 16-byte vectors into it)."""
+    d = _permute_desc(padded_mode=1, num_tokens=8192, num_experts=64, num_out_rows=64 * 512, capacity=512)
+    st, n = _pws(d)
+    assert st == 0 and n > 0
+    for off in (4, 16, 128):
+        assert F.lib().moe_permute(ctypes.byref(d), ctypes.c_void_p(FAKE + off), ctypes.c_size_t(n + 256),
+                                   None) == F.FFNWB_ERR_WORKSPACE
+    b = _batching_desc(A=64, BS=64, K1=9, H=7168, expert_num=1024, layer_num=16)
+    st, n = _bws(b)
+    assert st == 0 and n > 0
+    assert F.lib().ffnwb_batching(ctypes.byref(b), ctypes.c_void_p(FAKE + 8), ctypes.c_size_t(n + 256),
+                                  None) == F.FFNWB_ERR_WORKSPACE
+    u = _unpermute_desc()
+    st, n = _uws(u)
+    if n > 0:
+        assert F.lib().moe_unpermute(ctypes.byref(u), ctypes.c_void_p(FAKE + 64), ctypes.c_size_t(n + 256),
+                                     None) == F.FFNWB_ERR_WORKSPACE
 
 
 # ----------------------------------------------------------------------------- expert update

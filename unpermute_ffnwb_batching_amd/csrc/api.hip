@@ -24,6 +24,13 @@ void log_warn(const char* fmt, ...) {
   va_end(ap);
 }
 
+// The caller's workspace: at least `need` bytes, and (when any is needed) non-NULL and
+// 256-byte aligned, since the kernels store 16-byte vectors into the pieces carved from it.
+static bool workspace_ok(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return false;
+  return need == 0 || (ws != nullptr && reinterpret_cast<uintptr_t>(ws) % 256 == 0);
+}
+
 }  // namespace ffnwb
 
 using namespace ffnwb;
@@ -48,7 +55,7 @@ const char* ffnwb_status_string(int status) {
     case FFNWB_ERR_PARAM_NULLPTR: return "FFNWB_ERR_PARAM_NULLPTR: a required pointer is NULL";
     case FFNWB_ERR_PARAM_INVALID: return "FFNWB_ERR_PARAM_INVALID: a type, shape or range is not supported";
     case FFNWB_ERR_INNER_NULLPTR: return "FFNWB_ERR_INNER_NULLPTR: topK > 512 or unsupported probs shape";
-    case FFNWB_ERR_WORKSPACE: return "FFNWB_ERR_WORKSPACE: workspace missing or smaller than required";
+    case FFNWB_ERR_WORKSPACE: return "FFNWB_ERR_WORKSPACE: workspace missing, smaller than required or not 256-byte aligned";
     case FFNWB_ERR_RUNTIME: return "FFNWB_ERR_RUNTIME: the HIP runtime rejected a launch";
     default: return "unknown ffnwb status";
   }
@@ -67,7 +74,7 @@ int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_byte
   BatchingPlan p;
   const int st = plan_batching(d, &p);
   if (st != FFNWB_OK) return st;
-  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, ws_bytes, p.ws_bytes)) return FFNWB_ERR_WORKSPACE;
   return launch_batching(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -84,7 +91,7 @@ int ffnwb_batching_ctx(const ffnwb_batching_ctx_desc* d, void* workspace, size_t
   BatchingCtxPlan p;
   const int st = plan_batching_ctx(d, &p);
   if (st != FFNWB_OK) return st;
-  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, ws_bytes, p.ws_bytes)) return FFNWB_ERR_WORKSPACE;
   return launch_batching_ctx(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -101,7 +108,7 @@ int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes,
   UnpermutePlan p;
   const int st = plan_unpermute(d, &p);
   if (st != FFNWB_OK) return st;
-  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, ws_bytes, p.ws_bytes)) return FFNWB_ERR_WORKSPACE;
   return launch_unpermute(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -118,7 +125,7 @@ int moe_permute(const moe_permute_desc* d, void* workspace, size_t ws_bytes, voi
   PermutePlan p;
   const int st = plan_permute(d, &p);
   if (st != FFNWB_OK) return st;
-  if (ws_bytes < p.ws_bytes || (p.ws_bytes > 0 && workspace == nullptr)) return FFNWB_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, ws_bytes, p.ws_bytes)) return FFNWB_ERR_WORKSPACE;
   return launch_permute(d, p, workspace, static_cast<hipStream_t>(stream));
 }
 

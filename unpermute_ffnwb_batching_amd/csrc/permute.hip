@@ -13,15 +13,19 @@
 //        non-padded  row r = start[e] + (entries of column e in earlier tiles) + (entries
 //                    of column e in earlier rows of this tile); source_of[r] = t;
 //        padded      position j of the entry within expert e's capacity block;
-//                    sorted_indices[e*C + j] = t while j < C.
+//                    sorted_indices[e*C + j] = t while j < C, and the capacity row
+//                    e*C + j (or -1) of every (t, e) in a [T][E] table.
 //      Non-padded, a token's rows rise with its expert (rows are expert-major), so its
 //      slots are its entries in ascending expert order: each row of the tile is walked
 //      once more, and slot k takes the row of the k-th entry, whose offset inside the tile
 //      was kept in LDS (one byte per row and expert);
-//   3. non-padded: permute_scatter_kernel reads each token row once and writes it to every
-//      row its slots list, and fills the rows no slot lists (zero rows past the non-zero
-//      entries, rows of experts beyond a token's topK); padded: permute_rows_kernel, one
-//      wavefront per output row copying its source token row or writing zeros.
+//   3. permute_scatter_kernel reads each token row once and writes it to every row its
+//      list names (non-padded: its topK slots; padded: its row of the table), and fills the
+//      rows no list names (non-padded: zero rows past the non-zero entries and rows of
+//      experts beyond a token's topK; padded: zero rows of unused capacity).  Reading the
+//      token row once per output row instead (one wavefront per output row) read each
+//      padded token row once per expert it is routed to: 121.7 us for the row moves at
+//      E=64, C=512, T=8192, H=5120 FP16 with 4 experts per token.
 #include <stdio.h>
 
 #include "internal.hpp"
@@ -42,28 +46,46 @@ inline size_t permute_order_lds_bytes(int ntiles, int E, bool padded) {
 
 // Places the non-zero entries of NR consecutive rows (rows rbase .. rbase+NR-1 of group g)
 // of one work item, in row order, from the running offsets off[w] of its W columns.
+// Padded, every (row, column) of the item also gets its capacity row in dest ([T][E],
+// -1 where the entry is zero or past the capacity).
 template <int W, bool PADDED, int NR>
 __device__ __forceinline__ void permute_place_rows(const uint32_t (&xr)[NR], int rbase, int g, int c, int64_t t0,
                                                    int64_t T, int32_t E, const uint32_t* base, uint32_t (&off)[W],
                                                    int64_t N, int64_t C, int32_t* __restrict__ source_of,
-                                                   int32_t* __restrict__ sorted_indices, uint8_t* inoff) {
+                                                   int32_t* __restrict__ sorted_indices, uint8_t* inoff,
+                                                   int32_t* __restrict__ dest) {
   const int64_t r0 = t0 + g * kMaskGroupRows + rbase;
   uint32_t bs[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) bs[w] = base[c * W + w];  // read once, outside the per-entry branches
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
+    if (PADDED) {
+      int32_t dv[W];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const bool nz = r0 + r < T && ((xr[r] >> (8 * w)) & 0xffu) != 0;
+        const int e = c * W + w;
+        const uint32_t place = bs[w] + off[w];
+        const bool kept = nz && place < static_cast<uint64_t>(C);
+        dv[w] = kept ? static_cast<int32_t>(e * C + place) : -1;
+        if (kept) sorted_indices[e * C + place] = static_cast<int32_t>(r0 + r);
+        off[w] += nz ? 1u : 0u;
+      }
+      if (r0 + r < T) {
+        int32_t* drow = dest + (r0 + r) * E + c * W;
+        if (W == 4) *reinterpret_cast<int4*>(drow) = make_int4(dv[0], dv[W > 1 ? 1 : 0], dv[W > 2 ? 2 : 0], dv[W - 1]);
+        else drow[0] = dv[0];
+      }
+      continue;
+    }
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       if (r0 + r < T && ((xr[r] >> (8 * w)) & 0xffu) != 0) {
         const int e = c * W + w;
         const uint32_t place = bs[w] + off[w];
-        if (PADDED) {
-          if (place < static_cast<uint64_t>(C)) sorted_indices[e * C + place] = static_cast<int32_t>(r0 + r);
-        } else {
-          if (place < static_cast<uint64_t>(N)) source_of[place] = static_cast<int32_t>(r0 + r);
-          inoff[(g * kMaskGroupRows + rbase + r) * E + e] = static_cast<uint8_t>(off[w]);
-        }
+        if (place < static_cast<uint64_t>(N)) source_of[place] = static_cast<int32_t>(r0 + r);
+        inoff[(g * kMaskGroupRows + rbase + r) * E + e] = static_cast<uint8_t>(off[w]);
         ++off[w];
       }
     }
@@ -76,7 +98,8 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
                                                                         const uint32_t* __restrict__ hist,
                                                                         int64_t N, int32_t K, int64_t C,
                                                                         int32_t* __restrict__ source_of,
-                                                                        int32_t* __restrict__ sorted_indices) {
+                                                                        int32_t* __restrict__ sorted_indices,
+                                                                        int32_t* __restrict__ dest) {
   constexpr int NT = kPermuteThreads;
   extern __shared__ uint32_t lds[];
   uint32_t* h = lds;                     // [ntiles][E] tile histogram
@@ -166,7 +189,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
     }
     if (act)
       permute_place_rows<W, PADDED, kHalf>(x, hf * kHalf, g, c, t0, T, E, base, off, N, C, source_of, sorted_indices,
-                                           inoff);
+                                           inoff, dest);
   } else {
     for (int it = tid; it < items; it += NT) {
       const int g = it / cu;
@@ -177,7 +200,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
 #pragma unroll
       for (int w = 0; w < W; ++w) off[w] = gc[g * E + c * W + w];
       permute_place_rows<W, PADDED, kMaskGroupRows>(x, 0, g, c, t0, T, E, base, off, N, C, source_of,
-                                                    sorted_indices, inoff);
+                                                    sorted_indices, inoff, dest);
     }
   }
   if (PADDED) {
@@ -309,17 +332,18 @@ __device__ __forceinline__ void zero_row(uint8_t* __restrict__ dst, int64_t row_
   }
 }
 
-// Non-padded row moves.  Workgroups below token_blocks: one wavefront per token loads
-// each 16 KiB piece of the token's row once and stores it to every row its slots list
-// (sorted_indices[t*K .. t*K+K), -1 = none), with ordinary stores: this kernel writes K
-// times what it reads, and for such write-heavy traffic ordinary stores measured 4%
-// faster than non-temporal ones (242 vs 251 us at T=16384, topK=8, H=4096 BF16).  The
-// rest: one wavefront per 64 output rows handles the rows no slot lists:
-// source_of[r] = -1 (zeros) or -(t+2) (token t).
+// Row moves.  Workgroups below token_blocks: one wavefront per token loads each 16 KiB
+// piece of the token's row once and stores it to every row its list names
+// (lists[t*K .. t*K+K), -1 = none; K = topK non-padded, E padded), with ordinary stores:
+// this kernel writes several times what it reads, and for such write-heavy traffic
+// ordinary stores measured 4% faster than non-temporal ones (242 vs 251 us at T=16384,
+// topK=8, H=4096 BF16).  The rest: one wavefront per 64 output rows handles the rows no
+// list names: source_of[r] = -1 (zeros) or -(t+2) (token t); rows with source_of[r] >= 0
+// are the token wavefronts'.
 template <int VEC>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
                                                               int64_t row_bytes,
-                                                              const int32_t* __restrict__ sorted_indices, int64_t T,
+                                                              const int32_t* __restrict__ lists, int64_t T,
                                                               int32_t K, const int32_t* __restrict__ source_of,
                                                               int64_t N, unsigned token_blocks,
                                                               uint8_t* __restrict__ out) {
@@ -331,7 +355,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __r
     const uint8_t* src = tokens + t * stride;
     const int64_t n16 = row_bytes >> 4;
     for (int k0 = 0; k0 < K; k0 += kWave) {
-      const int32_t d = (k0 + static_cast<int>(lane) < K) ? sorted_indices[t * K + k0 + lane] : -1;
+      const int32_t d = (k0 + static_cast<int>(lane) < K) ? lists[t * K + k0 + lane] : -1;
       const uint64_t m = wave_ballot(d >= 0);
       if (m == 0) continue;
       if (VEC == 1) {
@@ -384,20 +408,6 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __r
   }
 }
 
-// One wavefront per output row: the source token's row, or zeros.
-template <int VEC>
-__global__ __launch_bounds__(256) void permute_rows_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
-                                                           int64_t row_bytes, const int32_t* __restrict__ source_of,
-                                                           int64_t N, uint8_t* __restrict__ out) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
-  if (r >= N) return;
-  const int32_t src = uniform(source_of[r]);
-  const uint32_t lane = lane_id();
-  uint8_t* dst = out + r * row_bytes;
-  if (src >= 0) copy_row<VEC>(tokens + static_cast<int64_t>(src) * stride, dst, row_bytes, lane);
-  else zero_row<VEC>(dst, row_bytes, lane);
-}
-
 static int element_bytes(int dtype) {
   switch (dtype) {
     case FFNWB_DT_FP16: case FFNWB_DT_BF16: return 2;
@@ -441,6 +451,7 @@ int plan_permute(const moe_permute_desc* d, PermutePlan* p) {
   Carve c;
   c.take<uint32_t>(static_cast<size_t>(ntiles * E));       // tile histogram
   if (!p->padded) c.take<int32_t>(static_cast<size_t>(N));  // source token of every row
+  else c.take<int32_t>(static_cast<size_t>(T * E));         // capacity row of every entry
   p->ws_bytes = c.off;
   return FFNWB_OK;
 }
@@ -451,6 +462,7 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   c.base = static_cast<char*>(ws);
   uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.ntiles * p.E));
   int32_t* source_of = p.padded ? d->sorted_indices : c.take<int32_t>(static_cast<size_t>(p.N));
+  int32_t* dest = p.padded ? c.take<int32_t>(static_cast<size_t>(p.T * p.E)) : nullptr;
   const uint8_t* map = d->routing_map;
   const int32_t E = static_cast<int32_t>(p.E);
   const int nt = static_cast<int>(p.ntiles);
@@ -463,7 +475,7 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
     hipLaunchKernelGGL(mask_tile_count_kernel<W>, dim3(nt, mask_ranges(E, W)), dim3(kMaskSplitThreads), 0, s, map,
                        p.T, E, hist, static_cast<uint32_t*>(nullptr));
     hipLaunchKernelGGL((permute_order_kernel<W, PADDED>), dim3(nt), dim3(kPermuteThreads), lds, s, map, p.T, E, nt,
-                       hist, p.N, static_cast<int32_t>(p.K), d->capacity, source_of, d->sorted_indices);
+                       hist, p.N, static_cast<int32_t>(p.K), d->capacity, source_of, d->sorted_indices, dest);
   };
   if (wide) {
     if (p.padded) go(std::integral_constant<int, 4>(), std::true_type());
@@ -475,38 +487,28 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
   const int vec = vec_class(reinterpret_cast<uintptr_t>(d->tokens), reinterpret_cast<uintptr_t>(d->permuted_tokens),
                             p.stride, p.row_bytes, p.row_bytes);
-  const unsigned blocks = static_cast<unsigned>((p.N + 3) / 4);
   const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
   uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
   // the optional hooks are bound to the row-copy launch
   void* evb = d->ev_copy_begin;
   void* eve = d->ev_copy_end;
+  // token rows to their rows: non-padded through the topK slots (rows past them through
+  // source_of), padded through the [T][E] table (zero rows are sorted_indices' -1 entries)
+  const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
+  const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
+  const int32_t K = static_cast<int32_t>(p.padded ? p.E : p.K);
+  const int32_t* lists = p.padded ? dest : d->sorted_indices;
+  const int32_t* src = source_of;
   bool ok;
-  if (!p.padded) {
-    const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
-    const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
-    const int32_t K = static_cast<int32_t>(p.K);
-    const int32_t* sorted = d->sorted_indices;
-    const int32_t* src = source_of;
-    if (vec == 16)
-      ok = launch_bound(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
-    else if (vec == 4)
-      ok = launch_bound(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
-    else
-      ok = launch_bound(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                        p.row_bytes, sorted, p.T, K, src, p.N, tb, out);
-  } else if (vec == 16) {
-    ok = launch_bound(permute_rows_kernel<16>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
-                      static_cast<const int32_t*>(source_of), p.N, out);
-  } else if (vec == 4) {
-    ok = launch_bound(permute_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
-                      static_cast<const int32_t*>(source_of), p.N, out);
-  } else {
-    ok = launch_bound(permute_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, evb, eve, tok, p.stride, p.row_bytes,
-                      static_cast<const int32_t*>(source_of), p.N, out);
-  }
+  if (vec == 16)
+    ok = launch_bound(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
+  else if (vec == 4)
+    ok = launch_bound(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
+  else
+    ok = launch_bound(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
+                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
   if (!ok) return FFNWB_ERR_RUNTIME;
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }
