@@ -19,6 +19,12 @@ def test_named_workload_full_size():
     check_permute(case, run_permute(case))
 
 
+def test_padded_named_workload_full_size():
+    case = synth.permute_padded_config()
+    print("permute padded E=64 C=512 T=8192 H=5120 fp16", flush=True)
+    check_permute(case, run_permute(case))
+
+
 NONPAD = [
     # (T, K, E, H, dtype, route, row_pad, n_t override)
     (1, 1, 1, 8, synth.FP32, "uniform", 0, None),
@@ -56,6 +62,9 @@ PAD = [
     (300, 6, 1, 9, synth.INT8, 2),         # C = 1, byte copies
     (700, 64, 48, 128, synth.FP32, 4),     # three tiles
     (50, 5, 0, 8, synth.FP16, 1),          # C = 0: nothing to write
+    (300, 256, 30, 16, synth.BF16, 200),   # up to 200 experts per token: four 64-entry table chunks
+    (150, 200, 64, 24, synth.FP16, 130),   # partial last table chunk (200 = 3*64 + 8)
+    (90, 130, 20, 8, synth.INT8, 100),     # E not a multiple of 4 (byte map loads) with partial chunks
 ]
 
 
