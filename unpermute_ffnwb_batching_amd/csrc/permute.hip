@@ -25,7 +25,8 @@
 //      experts beyond a token's topK; padded: zero rows of unused capacity).  Reading the
 //      token row once per output row instead (one wavefront per output row) read each
 //      padded token row once per expert it is routed to: 121.7 us for the row moves at
-//      E=64, C=512, T=8192, H=5120 FP16 with 4 experts per token.
+//      E=64, C=512, T=8192, H=5120 FP16 with 4 experts per token, against 77-84 us in
+//      token order.
 #include <stdio.h>
 
 #include "internal.hpp"
