@@ -34,8 +34,10 @@ Readings taken where the article is silent, garbled or self-contradictory
     accumulated, sort after every valid entry (stable), and get weight 0;
   * non-padded outIndex = stable argsort of sortedIndices with invalid slots
     (outside [0, rows)) first, and permuteTokenId = outIndex // topK -- the
-    only reading that fits the documented value ranges of both outputs
-    ("parity unpinned" beyond ranges, permutation and stability);
+    only reading that fits the documented value ranges of both outputs.  Where
+    the empty slots go (first) is the reading itself and stays unpinned; the
+    rest (order by row index, stability, an index >= rows counted as empty) is
+    pinned by a hand-worked example;
   * zero weights are multiplied in, not skipped, unless ``skip_zero_weight`` is set:
     then, as the article's kernel description has it (each slot's row is copied only
     when its index is valid and its prob is non-zero), terms with weight 0 are left
@@ -46,9 +48,11 @@ Pins (tests/test_oracle_unpermute.py): the article's padded {2,2} example
 (formula result; the article's printed "all 2" claim contradicts its own
 formula), closed forms (permute-then-unpermute identities, softmax-weighted
 recombination), brute force against torch index_add_ in float64 within the FP32
-error bound, property checks of the auxiliary outputs, and for the zero-weight
-skip: equality with the formula on finite rows and two worked examples where a
-zero-weight row holds NaN / inf.
+error bound, property checks of the auxiliary outputs, hand-worked examples of
+both weight indices on permuted (non-identity) sortedIndices, where W1 and W2
+give different sums, and of the non-padded auxiliary order with -1 and an index
+>= rows, and for the zero-weight skip: equality with the formula on finite rows
+and two worked examples where a zero-weight row holds NaN / inf.
 """
 
 import numpy as np

@@ -322,3 +322,43 @@ def test_zero_weight_skip_nonpadded_worked_example():
     assert out["unpermuted"].tolist() == [[4.0, 2.0], [4.0, 6.0]]
     plain = unpermute(x, nm.DT_FP32, sI, False, (2, 2), routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32)
     assert np.isnan(plain["unpermuted"][1]).all()
+
+
+# ------------------------------------------------------------------ hand-worked weight-index and order pins
+
+def test_W1_and_W2_worked_example_with_permuted_indices():
+    # Non-padded, T = 2 tokens, topK = 2 (N = 4), E = 2 experts, H = 2, FP32.
+    # routing map [[1, 1], [1, 0]], probs [[0.25, 0.75], [1.0, 0]]: the expert-major
+    # masked select lists (t0,e0), (t1,e0), (t0,e1), so P = [0.25, 1.0, 0.75, 0] (zero pad).
+    # sortedIndices = [2, 0, 1, -1]: token 0 reads rows 2 and 0, token 1 reads row 1.
+    x = np.array([[1, 2], [10, 20], [100, 200], [1000, 2000]], np.float32)
+    sI = np.array([2, 0, 1, -1], np.int32)
+    probs = np.array([[0.25, 0.75], [1.0, 0.0]], np.float32)
+    rmap = np.array([[1, 1], [1, 0]], np.int8)
+    kw = dict(routing_map=rmap, probs=probs, probs_dtype=nm.DT_FP32)
+    w2 = unpermute(x, nm.DT_FP32, sI, False, (2, 2), weight_index=0, **kw)
+    w1 = unpermute(x, nm.DT_FP32, sI, False, (2, 2), weight_index=1, **kw)
+    assert w2["permute_probs"].tolist() == [0.25, 1.0, 0.75, 0.0]
+    # W2, weight of the permuted row r = sI[i]: token 0 = x2*P[2] + x0*P[0]
+    # = [75, 150] + [0.25, 0.5]; token 1 = x1*P[1] = [10, 20]
+    assert w2["unpermuted"].tolist() == [[75.25, 150.5], [10.0, 20.0]]
+    # W1, weight of the slot i (the literal last line of branch 2): token 0 =
+    # x2*P[0] + x0*P[1] = [25, 50] + [1, 2]; token 1 = x1*P[2] = [7.5, 15]
+    assert w1["unpermuted"].tolist() == [[26.0, 52.0], [7.5, 15.0]]
+
+
+def test_nonpadded_aux_order_worked_example():
+    # Non-padded, T = 3, topK = 2 (N = rows = 6).  sortedIndices = [4, -1, 6, 1, 4, 0]:
+    # slot 1 holds -1 and slot 2 holds 6 = rows, both outside [0, rows), so both are empty
+    # slots.  Empty slots take the lowest key (the position of -1 is the design's reading,
+    # since -1 leaves the slot-index range unchanged); the others sort by row index.
+    # Keys [5, 0, 0, 2, 5, 1] -> stable order: slots 1, 2 (key 0), 5 (row 0), 3 (row 1),
+    # 0, 4 (row 4, in slot order).
+    x = np.arange(12, dtype=np.float32).reshape(6, 2)
+    sI = np.array([4, -1, 6, 1, 4, 0], np.int32)
+    out = unpermute(x, nm.DT_FP32, sI, False, (3, 2))
+    assert out["out_index"].tolist() == [1, 2, 5, 3, 0, 4]
+    assert out["permute_token_id"].tolist() == [0, 1, 2, 1, 0, 2]
+    # token 0 = x4 (slot 1 empty); token 1 = x1 (slot 2 out of range, skipped);
+    # token 2 = x4 + x0
+    assert out["unpermuted"].tolist() == [[8.0, 9.0], [2.0, 3.0], [8.0, 10.0]]
