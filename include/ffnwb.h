@@ -35,8 +35,10 @@
  *     returned, 256-byte aligned; FFNWB_ERR_WORKSPACE otherwise) and keeps it alive
  *     until the work on `stream` has finished.  Its contents on entry do not matter.
  *   - Inputs are read-only.  Inputs and outputs must not overlap.
- *   - Calls are stateless and may run concurrently on different streams with
- *     distinct workspaces and outputs.
+ *   - Calls are stateless: the library holds no stream, event, buffer or lock of its
+ *     own, so calls may run concurrently on different streams with distinct
+ *     workspaces and outputs, and never wait on each other.  (moe_unpermute may
+ *     also use an auxiliary stream and two events that the caller passes in.)
  *   - Every result is deterministic (bit-identical across runs).
  *   - Data errors inside arrays never fault: out-of-range ids / indices are
  *     treated as masked (batching) or skipped (unpermute), as documented below.
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FFNWB_ABI_VERSION 5
+#define FFNWB_ABI_VERSION 6
 
 /* Status codes.  The first three take the aclnn values both pages list. */
 #define FFNWB_OK                 0
@@ -166,8 +168,10 @@ int ffnwb_batching(const ffnwb_batching_desc* d, void* workspace, size_t ws_byte
  *
  * One call batches micro-batch m = polling_index of every session: slot s*n + j is entry
  * j of session s's chunk.  need_schedule = 1: a chunk whose flag is not 1 takes no part
- * (its slots count as masked; each flag is read once with an acquire load, nothing
- * waits).  need_schedule = 0: flags are not read.  From there the results are those of
+ * (its slots count as masked).  Each chunk's flag is read once, with an acquire load,
+ * then its layer id; every slot of the chunk follows that one read, so a flag that a
+ * producer sets during the call gives a chunk batched whole or not at all.  Nothing
+ * waits for a flag.  need_schedule = 0: flags are not read.  From there the results are those of
  * ffnwb_batching on the flattened slots, with session id s, micro-batch id m and token
  * id s*n + j.
  *
@@ -283,10 +287,26 @@ typedef struct moe_unpermute_desc {
      Applied in both layouts.  0 = off (formula-faithful, the default). */
   int32_t skip_zero_weight;
   int32_t reserved0;        /* must be 0 */
+
+  /* Optional auxiliary stream (hipStream_t, same device as `stream`) for the non-padded
+     out_index / permute_token_id sort, which depends on sorted_indices only.  NULL (or
+     equal to `stream`): the sort runs on `stream` with the rest of the call.  Otherwise
+     both events (hipEvent_t, created by the caller, best with hipEventDisableTiming) are
+     required: the library records aux_fork_event on `stream` (bound to the first kernel of
+     the call when there is one), makes aux_stream wait for it, enqueues the sort on
+     aux_stream, records aux_join_event there, and makes `stream` wait for it before the
+     call returns, so all of the call's work is ordered before later work on `stream`.
+     The events are re-recorded by every call: calls that may run at the same time must
+     not share them (calls issued one after another from one thread may).  Ignored in
+     padded mode and when out_index and permute_token_id are both NULL. */
+  void* aux_stream;
+  void* aux_fork_event;
+  void* aux_join_event;
 } moe_unpermute_desc;
 
 /* Validates *d and returns the workspace size in bytes (host only, no device work).
-   Errors: FFNWB_ERR_PARAM_NULLPTR (required pointer NULL), FFNWB_ERR_PARAM_INVALID
+   Errors: FFNWB_ERR_PARAM_NULLPTR (required pointer NULL, or aux_stream given without
+   both events), FFNWB_ERR_PARAM_INVALID
    (dtype combination, routing_map/probs NULL mismatch, num_rows != N, N not a multiple
    of T (non-padded) or of E (padded with probs), sizes out of range),
    FFNWB_ERR_INNER_NULLPTR (topK > 512, or num_experts outside (0, 8192] with probs). */

@@ -120,7 +120,7 @@ def oracle_unpermute(case, weight_index=0, skip_zero_weight=False):
         weight_index=weight_index, skip_zero_weight=skip_zero_weight)
 
 
-def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None, skip_zero_weight=False):
+def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None, skip_zero_weight=False, aux_stream=None):
     T, H = case["restore_shape"]
     N = case["sorted_indices"].shape[0]
     x = to_torch_elems(case["permuted"], case["dtype"])
@@ -134,7 +134,7 @@ def prepare_unpermute(case, weight_index=0, aux=True, ev_reduce=None, skip_zero_
         out["permute_probs"] = _canary((N,), probs.dtype)
     return F.UnpermuteCall(x, dev(case["sorted_indices"]), rmap, probs, padded_mode=case["padded_mode"],
                            restore_shape=(T, H), weight_index=weight_index, aux=aux, out=out, ev_reduce=ev_reduce,
-                           skip_zero_weight=skip_zero_weight)
+                           skip_zero_weight=skip_zero_weight, aux_stream=aux_stream)
 
 
 def fetch_unpermute(call, case):
@@ -244,15 +244,15 @@ def ctx_fields(area, info, data, polling):
                 token_data_buf=data.data_ptr(), token_data_buf_size=data.numel(), polling_index=polling)
 
 
-def prepare_ctx(area, polling, need_schedule, ctx_over=None, ev_gather=None, ptr_shift=None):
-    """Upload the data area and a context describing it (fields in ``ctx_over`` replaced,
-    pointer fields in ``ptr_shift`` moved by that many bytes); outputs pre-filled with
-    the canary."""
+def prepare_ctx(area, polling, need_schedule, ctx_over=None, ev_gather=None, ptr_shift=None, bufs=None):
+    """Upload the data area (or use the device buffers ``bufs`` = (info, data) already
+    holding it) and a context describing it (fields in ``ctx_over`` replaced, pointer
+    fields in ``ptr_shift`` moved by that many bytes); outputs pre-filled with the
+    canary."""
     A, BS, K1, H = area["A"], area["BS"], area["K1"], area["H"]
     Y = A * BS * K1
     td = area["token_dtype"]
-    info = dev(area["info"])
-    data = dev(area["data"].reshape(-1))
+    info, data = bufs if bufs is not None else (dev(area["info"]), dev(area["data"].reshape(-1)))
     f = ctx_fields(area, info, data, polling)
     f.update(ctx_over or {})
     for k, v in (ptr_shift or {}).items():

@@ -43,7 +43,7 @@ def test_descriptor_layout_and_version():
     assert L.moe_permute_desc_size() == ctypes.sizeof(F.PermuteDesc)
     assert L.ffnwb_batching_ctx_desc_size() == ctypes.sizeof(F.BatchingCtxDesc)
     assert L.moe_update_expert_desc_size() == ctypes.sizeof(F.UpdateExpertDesc)
-    assert F.ffnwb_abi_version() == 5
+    assert F.ffnwb_abi_version() == 6
     for st in (0, 161001, 161002, 561103, 1, 2):
         assert F.ffnwb_status_string(st).startswith("FFNWB_")
 
@@ -226,6 +226,14 @@ def test_unpermute_optional_outputs_may_be_null():
 ])
 def test_unpermute_invalid_parameters(over):
     assert _uws(_unpermute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+@pytest.mark.parametrize("missing", ["aux_fork_event", "aux_join_event"])
+def test_unpermute_aux_stream_needs_both_events(missing):
+    d = _unpermute_desc(aux_stream=FAKE, aux_fork_event=FAKE, aux_join_event=FAKE)
+    assert _uws(d)[0] == 0
+    setattr(d, missing, None)
+    assert _uws(d)[0] == F.FFNWB_ERR_PARAM_NULLPTR
 
 
 def test_unpermute_probs_without_map_is_invalid():

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from _gpu import check_ctx, fetch_batching, prepare_ctx, prepare_batching
+from _gpu import check_ctx, dev, fetch_batching, prepare_ctx, prepare_batching
 
 pytestmark = pytest.mark.gpu
 
@@ -124,3 +124,49 @@ def test_named_workload_shape_with_four_micro_batches():
     area = synth.schedule_area(12, 16, 4, 32, 9, 7168, 256, 1, synth.BF16, n_not_ready=12)
     print("context: A=16 M=4 BS=32 K+1=9 H=7168 bf16", flush=True)
     check_ctx(area, _run(area, 3, 1))
+
+
+def test_flags_set_during_the_decode_give_whole_chunks():
+    # A producer on a second stream rewrites every chunk's flag (a bounded run of copies of
+    # random 0/1 patterns) while batching calls run on the current stream, with no
+    # synchronisation between the two streams.  Whatever each call saw, every chunk must
+    # come out batched whole (all its slots, keyed with its own layer) or not at all.
+    A, BS, K1, H, E, Ln = 64, 16, 9, 8, 64, 4
+    n, El = BS * K1, E // Ln
+    area = synth.schedule_area(81, A, 1, BS, K1, H, E, Ln, synth.FP16)
+    words = area["info"].view(np.int32).reshape(A, 2 + n)
+    words[:, 1] = 1 + np.arange(A) % (Ln - 1)   # every chunk on a layer other than 0
+    info, data = dev(area["info"]), dev(area["data"].reshape(-1))
+    flags = info.view(torch.int32)[0::2 + n]
+    g = torch.Generator().manual_seed(5)
+    patterns = dev(torch.randint(0, 2, (64, A), generator=g, dtype=torch.int32).numpy())
+    calls = [prepare_ctx(area, 0, 1, bufs=(info, data)) for _ in range(48)]
+    prod = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("context: flags rewritten on a second stream during 48 calls", flush=True)
+    torch.cuda._sleep(50_000_000)          # both streams start together once this ends (bounded spin)
+    prod.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(prod):
+        for i in range(600):
+            flags.copy_(patterns[i % 64])
+    for c in calls:
+        c.run()
+    torch.cuda.synchronize()
+    ids = area["expert_ids"].reshape(A, n)
+    layer = words[:, 1]
+    seen = set()
+    for ci, c in enumerate(calls):
+        got = fetch_batching(c)
+        act = int(got["actual_token_num"][0])
+        tok = got["token_ids"][:act].astype(np.int64)
+        chunk = tok // n
+        counts = np.bincount(chunk, minlength=A)
+        assert set(np.unique(counts)) <= {0, n}, f"call {ci}: a chunk was batched in part"
+        seen.add(tuple(counts // n))
+        # the key of every output row, from group_list, against its chunk's layer and id
+        gl = got["group_list"]
+        key = np.repeat(gl[:, 0], gl[:, 1])[:act]
+        assert np.array_equal(key, layer[chunk] * El + ids[chunk, tok % n]), f"call {ci}: wrong keys"
+        assert np.array_equal(got["y"][:act], area["data"][tok]), f"call {ci}: wrong rows"
+        assert int(got["ctx_status"][0]) == 0 and int(got["err_count"][0]) == 0
+    print(f"distinct ready patterns seen: {len(seen)}", flush=True)

@@ -1,8 +1,10 @@
 """Calls on several streams at once, and calls captured in a HIP graph.
 
-  * two non-padded unpermutes (whose auxiliary order runs on the library's side
-    stream) and a batching, launched on three streams without synchronising between
-    them, each checked against the oracle;
+  * two non-padded unpermutes (one with its auxiliary order on a caller-supplied
+    auxiliary stream, one without) and a batching, launched on three streams without
+    synchronising between them, each checked against the oracle;
+  * a one-shot helper run on a side stream, its outputs and workspace allocated there,
+    followed by allocations on the current stream before that work has finished;
   * every entry point captured into one graph, replayed three times with new input
     data copied into the captured inputs (and eager work in between), every replay
     checked against the oracle for the data it saw.
@@ -27,7 +29,8 @@ def test_concurrent_calls_on_three_streams():
     u2 = synth.unpermute_nonpadded_case(32, T=1500, K=8, E=64, H=256, dtype=synth.FP16, probs_dtype=synth.FP16,
                                         n_empty=2000)
     bt = synth.batching_case(33, 16, 32, 9, 1024, 256, 1, synth.BF16, n_masked=300)
-    calls = [prepare_unpermute(u1), prepare_unpermute(u2), prepare_batching(bt)]
+    aux = torch.cuda.Stream()
+    calls = [prepare_unpermute(u1, aux_stream=aux), prepare_unpermute(u2), prepare_batching(bt)]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream() for _ in calls]
     print("three streams, no synchronisation between them", flush=True)
@@ -38,6 +41,38 @@ def test_concurrent_calls_on_three_streams():
     check_unpermute(u1, fetch_unpermute(calls[0], u1))
     check_unpermute(u2, fetch_unpermute(calls[1], u2))
     check_batching(bt, fetch_batching(calls[2]))
+
+
+def test_one_shot_helper_on_a_side_stream():
+    # The helper allocates its workspace on the stream it runs on.  The side stream is
+    # held back by a bounded spin, so the call's kernels run late; the current stream
+    # meanwhile allocates and fills buffers of the workspace's size.  Had the workspace
+    # been taken from the current stream's pool and freed on return, those buffers could
+    # reuse it while the call still writes there.
+    import unpermute_ffnwb_batching_amd as F
+    case = synth.unpermute_nonpadded_case(34, T=4096, K=8, E=64, H=1024, dtype=synth.BF16, probs_dtype=synth.FP32,
+                                          n_empty=3000)
+    x = dev(case["permuted"].view(np.int16)).view(torch.bfloat16)
+    sI, rmap, probs = dev(case["sorted_indices"]), dev(case["routing_map"]), dev(case["probs"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    kw = dict(padded_mode=False, restore_shape=(4096, 1024))
+    with torch.cuda.stream(side):
+        ws_bytes = F.UnpermuteCall(x, sI, rmap, probs, **kw).ws_bytes
+    assert ws_bytes > 0
+    print(f"one-shot unpermute on a side stream (workspace {ws_bytes} B), then allocations on the current "
+          "stream", flush=True)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    out = F.moe_unpermute(x, sI, rmap, probs, stream=side, **kw)
+    junk = [torch.full((ws_bytes,), 7, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    got = {"unpermuted": out["unpermuted"].view(torch.int16).cpu().numpy().view(np.uint16),
+           "out_index": out["out_index"].cpu().numpy(), "permute_token_id": out["permute_token_id"].cpu().numpy(),
+           "permute_probs": out["permute_probs"].cpu().numpy()}
+    check_unpermute(case, got)
+    assert all(int(j.min()) == 7 == int(j.max()) for j in junk)
 
 
 def _refill(t, a):
@@ -63,7 +98,9 @@ def test_every_entry_point_in_one_graph_replayed_with_new_inputs():
         )
 
     c0 = cases(seeds[0])
-    calls = dict(bt=prepare_batching(c0["bt"]), un=prepare_unpermute(c0["un"]), up=prepare_unpermute(c0["up"]),
+    aux = torch.cuda.Stream()
+    calls = dict(bt=prepare_batching(c0["bt"]), un=prepare_unpermute(c0["un"], aux_stream=aux),
+                 up=prepare_unpermute(c0["up"]),
                  pm=prepare_permute(c0["pm"]), ue=prepare_update_expert(c0["ue"]),
                  cx=prepare_ctx(c0["cx"], 2, 1))
     torch.cuda.synchronize()

@@ -21,6 +21,7 @@ The library must be built (``python -m unpermute_ffnwb_batching_amd.build``); im
 works without it, but every call then raises ``RuntimeError``: there is no fallback.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -126,6 +127,61 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocate under ``stream`` (the caching allocator then ties the blocks to it)."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _alloc_stream(device):
+    return torch.cuda.current_stream(device) if device.type == "cuda" else None
+
+
+def _record_on(tensors, stream, alloc_stream):
+    """Mark tensors as used by ``stream`` when it is not the stream they were allocated
+    on, so that the allocator does not hand their memory out before that work ends."""
+    if stream is None or alloc_stream is None or stream == alloc_stream:
+        return
+    for t in tensors:
+        if t is not None and t.numel() > 0:
+            t.record_stream(stream)
+
+
+# ----------------------------------------------------------------------------- argument checks
+# The C descriptors carry raw pointers and sizes only, so the shapes, element types and
+# layouts of the tensors behind them are checked here before any call is built.
+
+def _req(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name, device, dtypes=None, shape=None, contiguous=True):
+    _req(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _req(t.device == device, f"{name} is on {t.device}, expected {device}")
+    if dtypes is not None:
+        _req(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if shape is not None:
+        _req(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contiguous:
+        _req(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_numel(t, name, device, dtypes, numel):
+    _check_tensor(t, name, device, dtypes)
+    _req(t.numel() == numel, f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _span_bytes(t):
+    """Bytes from t's first element to just past its last (0 for an empty tensor)."""
+    if t.numel() == 0:
+        return 0
+    return (sum((n - 1) * st for n, st in zip(t.shape, t.stride())) + 1) * t.element_size()
+
+
+_I32 = (torch.int32,)
+_BYTES = (torch.uint8, torch.int8, torch.bool)
+
+
 # ----------------------------------------------------------------------------- batching
 
 _TOKEN_TORCH = {FFNWB_DT_FP16: torch.float16, FFNWB_DT_BF16: torch.bfloat16, FFNWB_DT_INT8: torch.int8}
@@ -165,6 +221,9 @@ class BatchingCall:
         out = dict(out or {})
         i32 = dict(dtype=torch.int32, device=dev)
         tdt = _TOKEN_TORCH.get(int(token_dtype), torch.uint8)
+        _check_batching_inputs(token_data, expert_ids, mask, layer_ids, session_ids, micro_batch_ids, token_scale,
+                               token_row_stride, scale_stride, A, Y, H, int(token_dtype))
+        _check_batching_outputs(out, dev, Y, H, int(expert_num), tdt)
         if "y" not in out:
             out["y"] = torch.empty((Y, H), dtype=tdt, device=dev)
         if "group_list" not in out:
@@ -180,6 +239,7 @@ class BatchingCall:
             out["err_count"] = torch.empty(1, **i32)
         self.out = out
         self._keep = [token_data, expert_ids, mask, layer_ids, session_ids, micro_batch_ids, token_scale]
+        self._alloc_stream = _alloc_stream(dev)
 
         d = BatchingDesc()
         d.A, d.BS, d.K1, d.H = A, BS, K1, H
@@ -224,12 +284,57 @@ class BatchingCall:
                                   _stream_handle(stream))
         if st != FFNWB_OK:
             raise FfnwbError(st, "ffnwb_batching")
+        _record_on([ws, *self.out.values()], stream, self._alloc_stream)
         return self.out
 
 
+def _check_batching_inputs(token_data, expert_ids, mask, layer_ids, session_ids, micro_batch_ids, token_scale,
+                           token_row_stride, scale_stride, A, Y, H, token_dtype):
+    _req(isinstance(token_data, torch.Tensor), "token_data must be a torch.Tensor")
+    dev = token_data.device
+    _req(token_dtype in _TOKEN_TORCH, f"token_dtype {token_dtype} is not FP16, BF16 or INT8")
+    _req(A > 0 and Y > 0 and H > 0, "max_out_shape entries must be positive")
+    _check_numel(expert_ids, "expert_ids", dev, _I32, Y)
+    if mask is not None:
+        _check_numel(mask, "mask", dev, _BYTES, Y)
+    for t, name in ((layer_ids, "layer_ids"), (session_ids, "session_ids"), (micro_batch_ids, "micro_batch_ids")):
+        if t is not None:
+            _check_numel(t, name, dev, _I32, A)
+    elt = 1 if token_dtype == FFNWB_DT_INT8 else 2
+    packed = token_dtype == FFNWB_DT_INT8 and token_scale is None
+    payload = H * elt + (4 if packed else 0)
+    stride = _row_stride_bytes(token_data) if token_row_stride is None else int(token_row_stride)
+    if stride == 0:
+        stride = payload
+    _req(stride >= payload, f"token row stride {stride} is below the row's {payload} bytes")
+    need = (Y - 1) * stride + payload
+    _req(_span_bytes(token_data) >= need,
+         f"token_data spans {_span_bytes(token_data)} bytes, the {Y} rows need {need}")
+    if token_scale is not None:
+        _check_tensor(token_scale, "token_scale", dev, (torch.float32,), contiguous=False)
+        sst = int(scale_stride) or 4
+        _req(_span_bytes(token_scale) >= (Y - 1) * sst + 4, "token_scale is too small for Y scales")
+
+
+def _check_batching_outputs(out, dev, Y, H, expert_num, tdt, ctx=False):
+    want = {"y": ((Y, H), (tdt,)), "group_list": ((expert_num, 2), (torch.int64,)),
+            "actual_token_num": ((1,), (torch.int64,)), "err_count": ((1,), _I32),
+            "dynamic_scale": ((Y,), (torch.float32,))}
+    if ctx:
+        want["ctx_status"] = ((1,), _I32)
+    for k in ("session_ids", "micro_batch_ids", "token_ids", "expert_offsets"):
+        want[k] = ((Y,), _I32)
+    for k, t in out.items():
+        _req(k in want, f"unknown output {k!r}")
+        shape, dtypes = want[k]
+        _check_tensor(t, f"out[{k!r}]", dev, dtypes, shape)
+
+
 def ffnwb_batching(token_data, expert_ids, *, stream=None, **kw):
-    """Run FFN-worker batching once; returns the dict of output tensors."""
-    return BatchingCall(token_data, expert_ids, **kw).run(stream)
+    """Run FFN-worker batching once on ``stream`` (default: the current stream); returns
+    the dict of output tensors, allocated on that stream."""
+    with _on(stream):
+        return BatchingCall(token_data, expert_ids, **kw).run(stream)
 
 
 def ffnwb_batching_ctx_workspace_size(desc):
@@ -256,6 +361,12 @@ class BatchingCtxCall:
         dev = schedule_context.device
         out = dict(out or {})
         i32 = dict(dtype=torch.int32, device=dev)
+        _req(int(token_dtype) in _TOKEN_TORCH, f"token_dtype {token_dtype} is not FP16, BF16 or INT8")
+        _req(A > 0 and Y > 0 and H > 0, "max_out_shape entries must be positive")
+        _check_tensor(schedule_context, "schedule_context", dev)
+        _req(schedule_context.numel() * schedule_context.element_size() >= FFNWB_CTX_BYTES,
+             f"schedule_context must hold {FFNWB_CTX_BYTES} bytes")
+        _check_batching_outputs(out, dev, Y, H, int(expert_num), _TOKEN_TORCH[int(token_dtype)], ctx=True)
         if "y" not in out:
             out["y"] = torch.empty((Y, H), dtype=_TOKEN_TORCH[int(token_dtype)], device=dev)
         if "group_list" not in out:
@@ -273,6 +384,7 @@ class BatchingCtxCall:
             out["ctx_status"] = torch.empty(1, **i32)
         self.out = out
         self._keep = [schedule_context]
+        self._alloc_stream = _alloc_stream(dev)
 
         d = BatchingCtxDesc()
         d.A, d.BS, d.K1, d.H = A, BS, K1, H
@@ -309,12 +421,15 @@ class BatchingCtxCall:
                                       _stream_handle(stream))
         if st != FFNWB_OK:
             raise FfnwbError(st, "ffnwb_batching_ctx")
+        _record_on([self.workspace, *self.out.values()], stream, self._alloc_stream)
         return self.out
 
 
 def ffnwb_batching_ctx(schedule_context, *, stream=None, **kw):
-    """Run FFN-worker batching from a ScheduleContext once; returns the output tensors."""
-    return BatchingCtxCall(schedule_context, **kw).run(stream)
+    """Run FFN-worker batching from a ScheduleContext once on ``stream`` (default: the
+    current stream); returns the output tensors, allocated on that stream."""
+    with _on(stream):
+        return BatchingCtxCall(schedule_context, **kw).run(stream)
 
 
 # ----------------------------------------------------------------------------- unpermute
@@ -336,16 +451,38 @@ class UnpermuteCall:
     ``permuted_tokens`` [rows, H] (fp16 / bf16 / fp32), ``sorted_indices`` int32 [N],
     ``routing_map`` int8/bool [T, E] or None, ``probs`` [T, E] or None.
     ``aux`` False skips out_index / permute_token_id.  ``skip_zero_weight`` leaves out
-    terms whose weight is 0 (opt-in; see include/ffnwb.h).
+    terms whose weight is 0 (opt-in; see include/ffnwb.h).  ``aux_stream`` (a
+    torch.cuda.Stream) runs the non-padded out_index / permute_token_id sort beside the
+    rest of the call; the call owns the two events that fork and join it, so calls that
+    may overlap need Call objects of their own.
     """
 
     def __init__(self, permuted_tokens, sorted_indices, routing_map=None, probs=None, *, padded_mode,
                  restore_shape, weight_index=0, aux=True, out=None, workspace=None, ev_reduce=None,
-                 skip_zero_weight=False):
+                 skip_zero_weight=False, aux_stream=None):
         T, H = (int(v) for v in restore_shape)
+        _check_tensor(permuted_tokens, "permuted_tokens", permuted_tokens.device, tuple(_FLOAT_CODE))
         dev = permuted_tokens.device
+        _req(permuted_tokens.dim() == 2, "permuted_tokens must be 2-D [rows, H]")
+        _req(T >= 0 and H == permuted_tokens.shape[1],
+             f"restore_shape {tuple(restore_shape)} does not match permuted_tokens' hidden size "
+             f"{permuted_tokens.shape[1]}")
+        _req(sorted_indices.dim() == 1, "sorted_indices must be 1-D")
+        _check_tensor(sorted_indices, "sorted_indices", dev, _I32)
+        _req((routing_map is None) == (probs is None), "routing_map and probs are given together or not at all")
+        if probs is not None:
+            _req(probs.dim() == 2 and probs.shape[0] == T, f"probs must be [T={T}, E]")
+            _check_tensor(probs, "probs", dev, tuple(_FLOAT_CODE))
+            _check_tensor(routing_map, "routing_map", dev, _BYTES, tuple(probs.shape))
         out = dict(out or {})
         N = sorted_indices.numel()
+        want = {"unpermuted": ((T, H), (permuted_tokens.dtype,)), "out_index": ((N,), _I32),
+                "permute_token_id": ((N,), _I32)}
+        if probs is not None:
+            want["permute_probs"] = ((N,), (probs.dtype,))
+        for k, t in out.items():
+            _req(k in want, f"unknown output {k!r}")
+            _check_tensor(t, f"out[{k!r}]", dev, want[k][1], want[k][0])
         if "unpermuted" not in out:
             out["unpermuted"] = torch.empty((T, H), dtype=permuted_tokens.dtype, device=dev)
         if aux:
@@ -359,6 +496,9 @@ class UnpermuteCall:
         if rm is not None and rm.dtype == torch.bool:
             rm = rm.view(torch.uint8)
         self._keep = [permuted_tokens, sorted_indices, rm, probs]
+        self._alloc_stream = _alloc_stream(dev)
+        self.aux_stream = aux_stream
+        self._aux_events = None
 
         d = UnpermuteDesc()
         d.dtype = _FLOAT_CODE.get(permuted_tokens.dtype, -1)
@@ -382,6 +522,13 @@ class UnpermuteCall:
         if ev_reduce is not None:
             d.ev_reduce_begin = _event_handle(ev_reduce[0])
             d.ev_reduce_end = _event_handle(ev_reduce[1])
+        if aux_stream is not None:
+            from .hip_events import HipEvent, HIP_EVENT_DISABLE_TIMING, HIP_EVENT_DISABLE_SYSTEM_FENCE
+            flags = HIP_EVENT_DISABLE_TIMING | HIP_EVENT_DISABLE_SYSTEM_FENCE
+            self._aux_events = (HipEvent(flags), HipEvent(flags))
+            d.aux_stream = ctypes.c_void_p(aux_stream.cuda_stream)
+            d.aux_fork_event = self._aux_events[0].handle
+            d.aux_join_event = self._aux_events[1].handle
         self.desc = d
         self.ws_bytes = moe_unpermute_workspace_size(d)
         if workspace is None and self.ws_bytes:
@@ -397,12 +544,19 @@ class UnpermuteCall:
                                  _stream_handle(stream))
         if st != FFNWB_OK:
             raise FfnwbError(st, "moe_unpermute")
+        _record_on([self.workspace, *self.out.values()], stream, self._alloc_stream)
+        if self.aux_stream is not None:
+            # the sort's workspace and outputs are also used on the auxiliary stream
+            _record_on([self.workspace, self.out.get("out_index"), self.out.get("permute_token_id")],
+                       self.aux_stream, self._alloc_stream)
         return self.out
 
 
 def moe_unpermute(permuted_tokens, sorted_indices, routing_map=None, probs=None, *, stream=None, **kw):
-    """Run the unpermute once; returns dict(unpermuted, out_index, permute_token_id, permute_probs)."""
-    return UnpermuteCall(permuted_tokens, sorted_indices, routing_map, probs, **kw).run(stream)
+    """Run the unpermute once on ``stream`` (default: the current stream); returns
+    dict(unpermuted, out_index, permute_token_id, permute_probs), allocated on that stream."""
+    with _on(stream):
+        return UnpermuteCall(permuted_tokens, sorted_indices, routing_map, probs, **kw).run(stream)
 
 
 # ----------------------------------------------------------------------------- permute
@@ -429,11 +583,23 @@ class PermuteCall:
 
     def __init__(self, tokens, routing_map, *, padded_mode=False, num_out_rows=None, capacity=0, out=None,
                  workspace=None, ev_copy=None):
-        T, H = tokens.shape[0], tokens.shape[1]
-        E = routing_map.shape[1]
+        _req(isinstance(tokens, torch.Tensor) and tokens.dim() == 2, "tokens must be a 2-D tensor [T, H]")
         dev = tokens.device
+        _check_tensor(tokens, "tokens", dev, tuple(_ANY_CODE), contiguous=False)
+        _req(tokens.stride(1) == 1 and tokens.stride(0) >= tokens.shape[1],
+             "tokens rows must be dense (stride 1 along H) and must not overlap")
+        T, H = tokens.shape[0], tokens.shape[1]
+        _req(isinstance(routing_map, torch.Tensor) and routing_map.dim() == 2 and routing_map.shape[0] == T,
+             f"routing_map must be [T={T}, E]")
+        _check_tensor(routing_map, "routing_map", dev, _BYTES)
+        E = routing_map.shape[1]
+        _req(bool(padded_mode) or num_out_rows is not None, "num_out_rows is required in non-padded mode")
         N = int(E * capacity) if padded_mode else int(num_out_rows)
         out = dict(out or {})
+        want = {"permuted_tokens": ((N, H), (tokens.dtype,)), "sorted_indices": ((N,), _I32)}
+        for k, t in out.items():
+            _req(k in want, f"unknown output {k!r}")
+            _check_tensor(t, f"out[{k!r}]", dev, want[k][1], want[k][0])
         if "permuted_tokens" not in out:
             out["permuted_tokens"] = torch.empty((N, H), dtype=tokens.dtype, device=dev)
         if "sorted_indices" not in out:
@@ -441,6 +607,7 @@ class PermuteCall:
         self.out = out
         rm = routing_map.view(torch.uint8) if routing_map.dtype in (torch.bool, torch.int8) else routing_map
         self._keep = [tokens, rm]
+        self._alloc_stream = _alloc_stream(dev)
         d = PermuteDesc()
         d.dtype = _ANY_CODE.get(tokens.dtype, -1)
         d.padded_mode = int(bool(padded_mode))
@@ -472,12 +639,15 @@ class PermuteCall:
                                _stream_handle(stream))
         if st != FFNWB_OK:
             raise FfnwbError(st, "moe_permute")
+        _record_on([self.workspace, *self.out.values()], stream, self._alloc_stream)
         return self.out
 
 
 def moe_permute(tokens, routing_map, *, stream=None, **kw):
-    """Run the forward permute once; returns dict(permuted_tokens, sorted_indices)."""
-    return PermuteCall(tokens, routing_map, **kw).run(stream)
+    """Run the forward permute once on ``stream`` (default: the current stream); returns
+    dict(permuted_tokens, sorted_indices), allocated on that stream."""
+    with _on(stream):
+        return PermuteCall(tokens, routing_map, **kw).run(stream)
 
 
 # ----------------------------------------------------------------------------- expert update
@@ -537,5 +707,7 @@ class UpdateExpertCall:
 
 
 def moe_update_expert(expert_ids, eplb_table, *, stream=None, **kw):
-    """Run MoeUpdateExpert once; returns the dict of output tensors."""
-    return UpdateExpertCall(expert_ids, eplb_table, **kw).run(stream)
+    """Run MoeUpdateExpert once on ``stream`` (default: the current stream); returns the
+    dict of output tensors, allocated on that stream."""
+    with _on(stream):
+        return UpdateExpertCall(expert_ids, eplb_table, **kw).run(stream)

@@ -2,7 +2,7 @@
 
 import ctypes
 
-FFNWB_ABI_VERSION = 5
+FFNWB_ABI_VERSION = 6
 
 FFNWB_OK = 0
 FFNWB_ERR_PARAM_NULLPTR = 161001
@@ -66,6 +66,7 @@ class UnpermuteDesc(ctypes.Structure):
         ("permute_probs", _vp),
         ("ev_reduce_begin", _vp), ("ev_reduce_end", _vp),
         ("skip_zero_weight", _i32), ("reserved0", _i32),
+        ("aux_stream", _vp), ("aux_fork_event", _vp), ("aux_join_event", _vp),
     ]
 
 

@@ -52,40 +52,42 @@ __device__ __forceinline__ uint32_t ctx_check(const CtxDecodeArgs& a, uint32_t M
   return st;
 }
 
-// One thread per slot g = s * n + j (entry j of session s's chunk at the polling index).
-// The thread of entry 0 also writes its chunk's layer id, micro-batch id and row address.
+// One workgroup per session s; its threads decode the entries j of session s's chunk at the
+// polling index.  Thread 0 reads the chunk's flag once (an acquire load, when
+// need_schedule is 1), then the chunk's layer id, which it writes out itself; it hands the
+// decision to the workgroup through LDS: every slot of the chunk takes that one decision, so a flag that a producer sets
+// while the decode runs gives a chunk that is batched whole or not at all, never a part
+// of it.  The other threads read the chunk's expert ids after the workgroup barrier, so
+// after the acquire.
 __global__ __launch_bounds__(kCtxThreads) void ctx_decode_kernel(CtxDecodeArgs a) {
+  __shared__ int32_t s_ready;
   const uint32_t M = reinterpret_cast<const uint32_t*>(a.ctx)[1];
   const uint64_t* ffn = reinterpret_cast<const uint64_t*>(a.ctx + kCtxFfnArea);
   const uint64_t info = ffn[0], info_size = ffn[1], data = ffn[2], data_size = ffn[3], polling = ffn[4];
   const uint32_t st = ctx_check(a, M, info, info_size, data, data_size, polling);
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kCtxThreads + threadIdx.x;
-  if (g == 0) *a.status = static_cast<int32_t>(st);
-  if (g >= a.A * a.n) return;
-  const int64_t s = g / a.n;
-  const int64_t j = g - s * a.n;
-  int32_t e = 0, layer = 0;
-  uint8_t masked = 1;
-  uint64_t src = 0;
-  if (st == 0) {
-    const uint64_t c = static_cast<uint64_t>(s) * M + polling;  // chunk number in the data area
-    int32_t* desc = reinterpret_cast<int32_t*>(info + c * (8 + 4 * static_cast<uint64_t>(a.n)));
-    // the flag is written by the sender: an acquire load orders this chunk's reads after it
-    const bool ready = a.need_schedule == 0 ||
-                       __hip_atomic_load(desc, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == 1;
-    if (ready) {
-      layer = desc[1];
-      e = desc[2 + j];
-      masked = 0;
+  const int64_t s = blockIdx.x;
+  const uint64_t c = static_cast<uint64_t>(s) * M + polling;  // chunk number in the data area
+  const int32_t* desc = reinterpret_cast<const int32_t*>(info + c * (8 + 4 * static_cast<uint64_t>(a.n)));
+  if (threadIdx.x == 0) {
+    int32_t ready = 0, layer = 0;
+    if (st == 0) {
+      // the flag is written by the sender: the acquire orders this chunk's reads after it
+      ready = a.need_schedule == 0 ||
+              __hip_atomic_load(const_cast<int32_t*>(desc), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == 1;
+      if (ready) layer = desc[1];
     }
-    src = data + c * static_cast<uint64_t>(a.n) * static_cast<uint64_t>(a.stride);
-  }
-  a.expert_ids[g] = e;
-  a.mask[g] = masked;
-  if (j == 0) {
+    s_ready = ready;
+    if (s == 0) *a.status = static_cast<int32_t>(st);
     a.layer_ids[s] = layer;
     a.micro_batch_ids[s] = st == 0 ? static_cast<int32_t>(polling) : 0;
-    a.chunk_src[s] = src;
+    a.chunk_src[s] = st == 0 ? data + c * static_cast<uint64_t>(a.n) * static_cast<uint64_t>(a.stride) : 0;
+  }
+  __syncthreads();
+  const bool ready = s_ready != 0;
+  for (int64_t j = threadIdx.x; j < a.n; j += kCtxThreads) {
+    const int64_t g = s * a.n + j;
+    a.expert_ids[g] = ready ? desc[2 + j] : 0;
+    a.mask[g] = ready ? 0 : 1;
   }
 }
 
@@ -172,8 +174,7 @@ int launch_batching_ctx(const ffnwb_batching_ctx_desc* d, const BatchingCtxPlan&
   a.micro_batch_ids = arr.micro_batch_ids;
   a.chunk_src = arr.chunk_src;
   a.status = d->ctx_status;
-  const unsigned blocks = static_cast<unsigned>((p.flat.Y + kCtxThreads - 1) / kCtxThreads);
-  hipLaunchKernelGGL(ctx_decode_kernel, dim3(blocks), dim3(kCtxThreads), 0, s, a);
+  hipLaunchKernelGGL(ctx_decode_kernel, dim3(static_cast<unsigned>(d->A)), dim3(kCtxThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
 
   ffnwb_batching_desc f;

@@ -10,8 +10,9 @@
 //            x * w in FP32 (slot order), one RNE store;
 //   [aux]    out_index / permute_token_id: stable sort of the slots by sortedIndices+1
 //            (LSD passes when the row count exceeds one pass's bucket budget), on the
-//            library's side stream, forked when the compaction's first kernel completes
-//            and joined after the reduce.
+//            caller's stream, or on the caller's auxiliary stream when the descriptor
+//            names one: forked when the compaction's first kernel completes and joined
+//            after the reduce.
 // Padded mode (branches 1 and 3):
 //   invert:  stable counting sort of the capacity entries by token id (rank, scan,
 //            scatter -> out_index, permute_token_id, permute_probs, per-token segments);
@@ -21,7 +22,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <mutex>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -485,45 +485,23 @@ static Placement run_passes_but_last_scatter(const SortPlan& sp, KS ks0, const S
   return pl;
 }
 
-// A library-owned stream per device on which the non-padded auxiliary sort runs, forked
-// from and joined back to the caller's stream with events, so that it overlaps the probs
-// compaction and the gather-reduce (it depends only on sortedIndices).  Created on first
-// use at the default priority; the mutex is held from a call's fork to its join wait,
-// so that no other call re-records the shared events in between.
-// Both streams live on one device, so the events skip the system-scope fence (a
-// device-scope release orders the side stream's writes for the caller's stream); with
-// the fence each record left the stream idle for several microseconds.
-struct SideStream {
+// The caller's auxiliary stream for the non-padded out_index / permute_token_id sort, with
+// the two events that fork it from and join it back to the caller's stream.  The library
+// keeps no stream or event of its own: without an auxiliary stream the sort runs on the
+// caller's stream, in order with the rest of the call.
+struct AuxFork {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr;
   hipEvent_t join = nullptr;
-  bool failed = false;
 };
-constexpr int kMaxDevices = 64;
-static std::mutex g_side_mu;
-static SideStream g_side[kMaxDevices];
 
-static SideStream* side_stream_for(hipStream_t caller) {
-  int dev = 0;
-  if (caller != nullptr) dev = hipGetStreamDeviceId(caller);
-  else if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  if (ss.stream == nullptr && !ss.failed) {
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    const bool switch_dev = cur != dev;
-    if (switch_dev) (void)hipSetDevice(dev);
-    constexpr unsigned kEvFlags = hipEventDisableTiming | hipEventDisableSystemFence;
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, kEvFlags) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, kEvFlags) != hipSuccess) {
-      ss.failed = true;
-      ss.stream = nullptr;
-    }
-    if (switch_dev) (void)hipSetDevice(cur);
-  }
-  return ss.failed ? nullptr : &ss;
+static AuxFork aux_fork_of(const moe_unpermute_desc* d, hipStream_t caller) {
+  AuxFork f;
+  if (d->aux_stream == nullptr || static_cast<hipStream_t>(d->aux_stream) == caller) return f;
+  f.stream = static_cast<hipStream_t>(d->aux_stream);
+  f.fork = static_cast<hipEvent_t>(d->aux_fork_event);
+  f.join = static_cast<hipEvent_t>(d->aux_join_event);
+  return f;
 }
 
 int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
@@ -539,6 +517,8 @@ int plan_unpermute(const moe_unpermute_desc* d, UnpermutePlan* p) {
   if (d->padded_mode != 0 && d->padded_mode != 1) return FFNWB_ERR_PARAM_INVALID;
   if (d->weight_index != 0 && d->weight_index != 1) return FFNWB_ERR_PARAM_INVALID;
   if ((d->skip_zero_weight != 0 && d->skip_zero_weight != 1) || d->reserved0 != 0) return FFNWB_ERR_PARAM_INVALID;
+  if (d->aux_stream != nullptr && (d->aux_fork_event == nullptr || d->aux_join_event == nullptr))
+    return FFNWB_ERR_PARAM_NULLPTR;
   if (d->hidden <= 0 || d->num_tokens < 0 || d->num_indices < 0 || d->num_rows < 0) return FFNWB_ERR_PARAM_INVALID;
   if (d->num_rows != d->num_indices) return FFNWB_ERR_PARAM_INVALID;
   const int64_t lim = (int64_t{1} << 31) - 2;
@@ -701,14 +681,13 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     SortBufs b{};
     const bool aux = p.need_aux && p.N > 0;
     if (aux) carve_sort_bufs(c, p.sort, p.N, &b);
-    // The auxiliary order (out_index / permute_token_id) runs on the side stream.  The
-    // lock covers the fork, the side stream's work and the caller stream's wait for the
-    // join, so that no other call re-records the shared events in between.
-    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
-    SideStream* side = nullptr;
+    // The auxiliary order (out_index / permute_token_id) runs on the caller's auxiliary
+    // stream when one is given, else on the caller's stream.
+    AuxFork side_f;
+    AuxFork* side = nullptr;
     if (aux) {
-      lock.lock();
-      side = side_stream_for(s);
+      side_f = aux_fork_of(d, s);
+      if (side_f.stream != nullptr) side = &side_f;
     }
     const bool fused = p.has_probs && nt > 0 && p.mask_fused;
     const uint8_t* map = d->routing_map;
@@ -734,10 +713,9 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     }
     if (aux) {
       hipStream_t as = s;
-      if (side != nullptr && forked && hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess) {
+      if (side != nullptr) {
+        if (!forked || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
         as = side->stream;
-      } else {
-        side = nullptr;  // the order runs on the caller's stream
       }
       KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
       const uint32_t *kin, *vin;

@@ -1,4 +1,5 @@
-"""Minimal HIP timing events for the library's timing hooks (plumbing only).
+"""Minimal HIP events for the library's timing hooks and the unpermute's auxiliary-stream
+fork and join (plumbing only).
 
 The descriptors' ev_* fields take hipEvent_t handles, which the library binds to the
 timed kernel's launch (or records on the stream under graph capture).  These events are
@@ -11,6 +12,7 @@ import ctypes
 import torch  # noqa: F401  (loads the HIP runtime first)
 
 _HIP = None
+HIP_EVENT_DISABLE_TIMING = 0x2
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
