@@ -405,8 +405,14 @@ def main():
     print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     calls = {}
+    # the non-padded call's out_index / permute_token_id sort runs on an auxiliary stream
+    # the caller owns (default priority), forked and joined inside the call
+    aux_stream = torch.cuda.Stream()
     for n, c in cases.items():
-        calls[n] = prepare_batching(c) if n.startswith("batching") else prepare_unpermute(c)
+        if n.startswith("batching"):
+            calls[n] = prepare_batching(c)
+        else:
+            calls[n] = prepare_unpermute(c, aux_stream=aux_stream if n == "unpermute_nonpadded" else None)
     torch.cuda.synchronize()
 
     # algorithmic bytes and rows per workload (actual_token_num from the first run)
@@ -522,6 +528,42 @@ def main():
                 parity = False
                 print(f"# parity FAILED for {n}: {ex}", file=sys.stderr, flush=True)
 
+    # workload 1 (tiny, latency-bound): call time in microseconds, flushed and warm
+    latency = None
+    if args.detail_iters > 0 and not args.only:
+        c1 = synth.batching_config(1)
+        call1 = prepare_batching(c1)
+        for _ in range(10):
+            call1.run(stream)
+        torch.cuda.synchronize()
+        act1 = int(call1.out["actual_token_num"].item())
+        ts = flushed_times(call1.run, stream, args.detail_iters)
+        warm = warm_ms(call1.run, stream, 100)
+        latency = {"batching_tiny": {
+            "shape": "A=2 BS=8 K+1=3 (Y=48) H=128 fp16, 16 experts, 5 slots masked",
+            "us_median": round(float(np.median(ts)) * 1e3, 2), "us_p10": round(float(np.percentile(ts, 10)) * 1e3, 2),
+            "us_p90": round(float(np.percentile(ts, 90)) * 1e3, 2), "iters": args.detail_iters,
+            "us_warm": round(warm * 1e3, 2), "rows": act1,
+            "rows_per_s": round(act1 / float(np.median(ts)) * 1e3, 1)}}
+        if not args.no_cpu_baseline:
+            from _gpu import oracle_batching
+            ref1 = oracle_batching(c1)
+            try:
+                check_batching(c1, fetch_batching(call1), ref1)
+                latency["batching_tiny"]["parity"] = True
+            except AssertionError as ex:
+                latency["batching_tiny"]["parity"] = False
+                print(f"# parity FAILED for the tiny batching: {ex}", file=sys.stderr, flush=True)
+        # the non-padded call with its auxiliary sort on the caller's stream (no aux stream)
+        if have_np:
+            c4 = cases["unpermute_nonpadded"]
+            call4 = prepare_unpermute(c4)
+            for _ in range(10):
+                call4.run(stream)
+            ts4 = flushed_times(call4.run, stream, args.detail_iters)
+            detail["unpermute_nonpadded"]["us_median_aux_on_caller_stream"] = round(float(np.median(ts4)) * 1e3, 2)
+            del call4
+
     roof = None
     if have_np:
         red_bytes = nonpadded_reduce_bytes(cases["unpermute_nonpadded"])
@@ -555,7 +597,7 @@ def main():
         "config": {"workload": "moe_reorder_suite: " + "+".join(names),
                    "step_alg_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
                    "element_types": "bf16/int8 rows moved; fp32 accumulation in unpermute"},
-        "roofline": roof, "cpu_baseline": cpu, "configs": detail, "parity": parity,
+        "roofline": roof, "cpu_baseline": cpu, "configs": detail, "latency": latency, "parity": parity,
         "next_rows": next_rows,
     }
     print(json.dumps(line), flush=True)
