@@ -38,7 +38,9 @@
  *   - Calls are stateless: the library holds no stream, event, buffer or lock of its
  *     own, so calls may run concurrently on different streams with distinct
  *     workspaces and outputs, and never wait on each other.  (moe_unpermute may
- *     also use an auxiliary stream and two events that the caller passes in.)
+ *     also use an auxiliary stream and two events that the caller passes in.)  The
+ *     one exception is moe_unpermute_noalloc, whose workspace is a device array the
+ *     library holds on each GPU.
  *   - Every result is deterministic (bit-identical across runs).
  *   - Data errors inside arrays never fault: out-of-range ids / indices are
  *     treated as masked (batching) or skipped (unpermute), as documented below.
@@ -66,6 +68,8 @@ extern "C" {
 #define FFNWB_ERR_INNER_NULLPTR  561103 /* unpermute: topK > 512, or probs has an unsupported shape */
 #define FFNWB_ERR_WORKSPACE      1      /* workspace NULL, smaller than the query returned, or not 256-byte aligned */
 #define FFNWB_ERR_RUNTIME        2      /* the HIP runtime refused a launch or a device query */
+#define FFNWB_ERR_SCRATCH        3      /* moe_unpermute_noalloc: the call needs more than
+                                           FFNWB_NOALLOC_SCRATCH_BYTES of workspace */
 
 /* Element types. 0..2 are the batching page's tokenDtype values. */
 #define FFNWB_DT_FP16 0
@@ -314,6 +318,21 @@ int moe_unpermute_workspace_size(const moe_unpermute_desc* d, size_t* ws_bytes);
 
 /* Validates again, then enqueues the unpermute on `stream`. */
 int moe_unpermute(const moe_unpermute_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc): moe_unpermute with its workspace taken
+   from a static device array the library holds on each GPU it runs on, of
+   FFNWB_NOALLOC_SCRATCH_BYTES, until the process ends.  The caller still passes every input
+   and output in *d.  Same validation, kernels and results as moe_unpermute; in addition
+   FFNWB_ERR_SCRATCH when moe_unpermute_workspace_size would return more than
+   FFNWB_NOALLOC_SCRATCH_BYTES (returned before any device work).  The call itself
+   allocates nothing; its first call on a GPU looks up that GPU's array address once.
+   All calls on one GPU share that GPU's array: calls that may overlap in time on one GPU
+   (on different streams, or from different threads) race and give undefined results;
+   calls ordered on one stream are safe.  The array's contents between calls do not
+   matter to the kernels. */
+#define FFNWB_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_unpermute_noalloc(const moe_unpermute_desc* d, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * MoE token permute with routing map: the step before the experts that the

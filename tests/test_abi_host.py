@@ -228,6 +228,16 @@ def test_unpermute_invalid_parameters(over):
     assert _uws(_unpermute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
 
 
+def test_unpermute_noalloc_rejects_calls_above_its_scratch_before_device_work():
+    # T = 131072, topK = 8, E = 256 with the auxiliary outputs needs 26.5 MiB of workspace
+    d = _unpermute_desc(num_tokens=131072, num_rows=131072 * 8, num_indices=131072 * 8, num_experts=256)
+    st, n = _uws(d)
+    assert st == 0 and n > F.FFNWB_NOALLOC_SCRATCH_BYTES
+    assert F.lib().moe_unpermute_noalloc(ctypes.byref(d), None) == F.FFNWB_ERR_SCRATCH
+    assert F.lib().moe_unpermute_noalloc(ctypes.byref(_unpermute_desc(dtype=7)), None) == F.FFNWB_ERR_PARAM_INVALID
+    assert F.ffnwb_status_string(F.FFNWB_ERR_SCRATCH).startswith("FFNWB_ERR_SCRATCH")
+
+
 @pytest.mark.parametrize("missing", ["aux_fork_event", "aux_join_event"])
 def test_unpermute_aux_stream_needs_both_events(missing):
     d = _unpermute_desc(aux_stream=FAKE, aux_fork_event=FAKE, aux_join_event=FAKE)

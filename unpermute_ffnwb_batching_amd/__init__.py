@@ -7,7 +7,7 @@ The names mirror the C ABI:
 
 * ``ffnwb_batching_workspace_size`` / ``ffnwb_batching``
 * ``ffnwb_batching_ctx_workspace_size`` / ``ffnwb_batching_ctx`` (ScheduleContext input)
-* ``moe_unpermute_workspace_size`` / ``moe_unpermute``
+* ``moe_unpermute_workspace_size`` / ``moe_unpermute`` / ``moe_unpermute_noalloc``
 * ``moe_permute_workspace_size`` / ``moe_permute``
 * ``moe_update_expert_workspace_size`` / ``moe_update_expert``
 * ``ffnwb_status_string``, ``ffnwb_abi_version``
@@ -29,7 +29,8 @@ import torch  # loads the HIP runtime the library binds to (same soname)
 
 from . import _abi
 from ._abi import (FFNWB_OK, FFNWB_ERR_PARAM_NULLPTR, FFNWB_ERR_PARAM_INVALID,  # noqa: F401
-                   FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME,
+                   FFNWB_ERR_INNER_NULLPTR, FFNWB_ERR_WORKSPACE, FFNWB_ERR_RUNTIME, FFNWB_ERR_SCRATCH,
+                   FFNWB_NOALLOC_SCRATCH_BYTES,
                    FFNWB_DT_FP16, FFNWB_DT_BF16, FFNWB_DT_INT8, FFNWB_DT_FP32,
                    FFNWB_CTX_BYTES, FFNWB_CTX_SHAPE, FFNWB_CTX_POLLING, FFNWB_CTX_POINTER,
                    FFNWB_CTX_BUFFER, FFNWB_DT_INT32, FFNWB_DT_INT64, BatchingDesc, BatchingCtxDesc,
@@ -60,13 +61,14 @@ def lib():
         L.ffnwb_batching_ctx.argtypes = [ctypes.POINTER(BatchingCtxDesc), vp, sz, vp]
         L.moe_unpermute_workspace_size.argtypes = [ctypes.POINTER(UnpermuteDesc), ctypes.POINTER(sz)]
         L.moe_unpermute.argtypes = [ctypes.POINTER(UnpermuteDesc), vp, sz, vp]
+        L.moe_unpermute_noalloc.argtypes = [ctypes.POINTER(UnpermuteDesc), vp]
         L.moe_permute_workspace_size.argtypes = [ctypes.POINTER(PermuteDesc), ctypes.POINTER(sz)]
         L.moe_permute.argtypes = [ctypes.POINTER(PermuteDesc), vp, sz, vp]
         L.moe_update_expert_workspace_size.argtypes = [ctypes.POINTER(UpdateExpertDesc), ctypes.POINTER(sz)]
         L.moe_update_expert.argtypes = [ctypes.POINTER(UpdateExpertDesc), vp, sz, vp]
         for f in ("ffnwb_batching_workspace_size", "ffnwb_batching", "ffnwb_batching_ctx_workspace_size",
                   "ffnwb_batching_ctx", "moe_unpermute_workspace_size",
-                  "moe_unpermute", "moe_permute_workspace_size", "moe_permute", "moe_update_expert_workspace_size",
+                  "moe_unpermute", "moe_unpermute_noalloc", "moe_permute_workspace_size", "moe_permute", "moe_update_expert_workspace_size",
                   "moe_update_expert", "ffnwb_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.ffnwb_status_string.argtypes = [ctypes.c_int]
@@ -454,7 +456,8 @@ class UnpermuteCall:
     terms whose weight is 0 (opt-in; see include/ffnwb.h).  ``aux_stream`` (a
     torch.cuda.Stream) runs the non-padded out_index / permute_token_id sort beside the
     rest of the call; the call owns the two events that fork and join it, so calls that
-    may overlap need Call objects of their own.
+    may overlap need Call objects of their own.  ``workspace=False`` allocates no
+    workspace, for a call that only runs through ``run_noalloc``.
     """
 
     def __init__(self, permuted_tokens, sorted_indices, routing_map=None, probs=None, *, padded_mode,
@@ -533,7 +536,15 @@ class UnpermuteCall:
         self.ws_bytes = moe_unpermute_workspace_size(d)
         if workspace is None and self.ws_bytes:
             workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
-        self.workspace = workspace
+        self.workspace = workspace if workspace is not False else None
+
+    def run_noalloc(self, stream=None):
+        """Runs the call through moe_unpermute_noalloc: the workspace is the library's
+        per-GPU scratch array, and nothing is allocated."""
+        st = lib().moe_unpermute_noalloc(ctypes.byref(self.desc), _stream_handle(stream))
+        if st != FFNWB_OK:
+            raise FfnwbError(st, "moe_unpermute_noalloc")
+        return self.out
 
     def set_reduce_events(self, begin, end):
         self.desc.ev_reduce_begin = _event_handle(begin)
@@ -550,6 +561,11 @@ class UnpermuteCall:
             _record_on([self.workspace, self.out.get("out_index"), self.out.get("permute_token_id")],
                        self.aux_stream, self._alloc_stream)
         return self.out
+
+
+def moe_unpermute_noalloc(call, stream=None):
+    """Runs a prepared UnpermuteCall through the no-allocation entry point."""
+    return call.run_noalloc(stream)
 
 
 def moe_unpermute(permuted_tokens, sorted_indices, routing_map=None, probs=None, *, stream=None, **kw):

@@ -10,6 +10,8 @@ FFNWB_ERR_PARAM_INVALID = 161002
 FFNWB_ERR_INNER_NULLPTR = 561103
 FFNWB_ERR_WORKSPACE = 1
 FFNWB_ERR_RUNTIME = 2
+FFNWB_ERR_SCRATCH = 3
+FFNWB_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 FFNWB_DT_FP16 = 0
 FFNWB_DT_BF16 = 1

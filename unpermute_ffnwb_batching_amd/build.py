@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libffnwb.so")
-SOURCES = ["api.hip", "batching.hip", "unpermute.hip", "permute.hip", "context.hip", "update_expert.hip"]
+SOURCES = ["api.hip", "batching.hip", "unpermute.hip", "permute.hip", "context.hip", "update_expert.hip",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -57,6 +57,8 @@ const char* ffnwb_status_string(int status) {
     case FFNWB_ERR_INNER_NULLPTR: return "FFNWB_ERR_INNER_NULLPTR: topK > 512 or unsupported probs shape";
     case FFNWB_ERR_WORKSPACE: return "FFNWB_ERR_WORKSPACE: workspace missing, smaller than required or not 256-byte aligned";
     case FFNWB_ERR_RUNTIME: return "FFNWB_ERR_RUNTIME: the HIP runtime rejected a launch";
+    case FFNWB_ERR_SCRATCH:
+      return "FFNWB_ERR_SCRATCH: the call needs more workspace than the no-allocation entry point holds";
     default: return "unknown ffnwb status";
   }
 }
