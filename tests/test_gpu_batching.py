@@ -32,6 +32,9 @@ RANDOM = [
     (64, 512, 9, 16, 256, 2, synth.FP16, 1000, 10, True, 0, False),    # Y = 294912: multi-launch sort
     (16, 64, 8, 32, 2048, 4, synth.BF16, 700, 11, True, 0, False),     # Y = 8192, 2048 keys: one-workgroup order at its limits
     (16, 32, 9, 64, 4096, 2, synth.FP16, 300, 5, True, 0, False),      # 4096 keys: range-partitioned order
+    (16, 128, 8, 64, 8192, 8, synth.BF16, 900, 7, True, 0, False),     # Y = 16384, 8192 keys: placement by 4096-slot tiles
+    (64, 128, 8, 16, 1024, 16, synth.INT8, 3000, 9, True, 0, False),   # Y = 65536: placement at its 64-tile limit
+    (65, 128, 8, 16, 512, 2, synth.FP16, 2000, 4, False, 0, False),    # Y = 66560: 65 tiles, rank / scan / gather
 ]
 
 

@@ -530,6 +530,145 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
   }
 }
 
+// Placement by tiles after sort_rank_kernel<KeyBatching>, for at most kPlaceMaxTiles
+// tiles; it replaces the one-workgroup histogram scan.  Workgroup t reads the whole
+// tile-major histogram (nt x nb words, in L2) and sums each key's column over all tiles
+// and over the tiles before t.  An exclusive scan of the sums gives each key's first
+// output row, so every workgroup places its own tile's slots without waiting for another:
+// inv[row] = slot.  Workgroup 0 writes every key's first row to kstart, group_list,
+// actual_token_num and err_count.  The row copy that follows walks the output rows
+// (random reads, sequential writes, which measured faster than walking the slots) and
+// writes the row IDs, in row order.
+// LDS: key sums -> first rows [nb] | sums before the tile [nb].
+constexpr int kPlaceMaxTiles = 64;
+
+template <int B>  // histogram loads in flight per thread: B >= nt walks a column in one round
+__global__ __launch_bounds__(kWgThreads) void batching_place_kernel(BatchArgs a, const uint32_t* __restrict__ packed,
+                                                                    const uint32_t* __restrict__ hist_g,
+                                                                    const uint32_t* __restrict__ tile_err, int nb,
+                                                                    int nt, int tile_shift,
+                                                                    uint32_t* __restrict__ inv,
+                                                                    uint32_t* __restrict__ kstart,
+                                                                    int64_t* __restrict__ group_list,
+                                                                    int64_t group_rows,
+                                                                    int64_t* __restrict__ actual,
+                                                                    int32_t* __restrict__ err_count) {
+  extern __shared__ uint32_t lds_words[];
+  __shared__ uint32_t wsum[2][2 * kWgWaves + 1];  // ping-pong: a scan's totals are read after it
+  uint32_t* cnt = lds_words;
+  uint32_t* bef = cnt + nb;
+  const int t = blockIdx.x;
+  const uint32_t Y = static_cast<uint32_t>(a.Y);
+  const uint32_t tile = 1u << tile_shift;
+  const uint32_t j0 = static_cast<uint32_t>(t) << tile_shift;
+  // the tile's packed ranks (at most 4 per thread), loaded before the histogram is walked
+  uint32_t pk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t j = j0 + r * kWgThreads + threadIdx.x;
+    pk[r] = (r * kWgThreads < static_cast<int>(tile) && j < Y) ? packed[j] : kNoRank;
+  }
+  // 1. per key: the sum over all tiles and over the tiles before t
+  for (int k = threadIdx.x; k < nb; k += kWgThreads) {
+    uint32_t all = 0, before = 0;
+    for (int u0 = 0; u0 < nt; u0 += B) {
+      uint32_t c[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) c[u] = hist_g[static_cast<int64_t>(min(u0 + u, nt - 1)) * nb + k];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int tu = u0 + u;
+        all += tu < nt ? c[u] : 0u;
+        before += tu < t ? c[u] : 0u;
+      }
+    }
+    cnt[k] = all;
+    bef[k] = before;
+  }
+  __syncthreads();
+  // 2. cnt[k] <- first output row of key k (one scan of [sums | presence]: the presence
+  //    prefix is offset by the sums' total); workgroup 0 writes kstart and group_list
+  const bool g0 = t == 0;
+  uint32_t carry = 0, gcarry = 0;
+  for (int k0 = 0, it = 0; k0 < nb; k0 += kWgThreads, it ^= 1) {
+    const int kk = k0 + threadIdx.x;
+    const uint32_t c = (kk < nb) ? cnt[kk] : 0u;
+    uint32_t v[2] = {c, c > 0 ? 1u : 0u};
+    uint32_t all;
+    block_exscan_multi<kWgThreads, 2>(v, wsum[it], all);
+    const uint32_t tot = wsum[it][kWgWaves];  // sequence 1 starts after all sums
+    if (kk < nb) cnt[kk] = carry + v[0];
+    if (g0 && kk < nb) kstart[kk] = carry + v[0];
+    if (g0 && c > 0) {
+      const int64_t slot = gcarry + v[1] - tot;
+      group_list[2 * slot] = kk;
+      group_list[2 * slot + 1] = c;
+    }
+    carry += tot;
+    gcarry += all - tot;
+  }
+  if (g0) {
+    for (int64_t g = gcarry + threadIdx.x; g < group_rows; g += kWgThreads) {
+      group_list[2 * g] = 0;
+      group_list[2 * g + 1] = 0;
+    }
+    uint32_t e = 0;
+    for (int u = threadIdx.x; u < nt; u += kWgThreads) e += tile_err[u];
+    e = wave_sum(e);
+    if (threadIdx.x == 0) {
+      *actual = static_cast<int64_t>(carry);
+      if (err_count != nullptr) *err_count = static_cast<int32_t>(e);  // nt <= 64: wave 0 holds them all
+    }
+  }
+  __syncthreads();  // first rows complete
+  // 3. place the tile's slots
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t p = pk[r];
+    if (p == kNoRank) continue;
+    const uint32_t d = p >> 16;
+    inv[cnt[d] + bef[d] + (p & 0xffffu)] = j0 + r * kWgThreads + threadIdx.x;
+  }
+}
+
+// Row copy after batching_place_kernel: one wavefront per output row below
+// actual_token_num, reading the row of slot inv[row].  Lane 0 writes the row IDs (the
+// slot's key from its packed rank, and the key's first row, are looked up while the row
+// loads are in flight); the INT8 scale moves with its row.
+template <int VEC>
+__global__ __launch_bounds__(256) void batching_copy_out_kernel(BatchArgs a, const uint32_t* __restrict__ inv,
+                                                                const uint32_t* __restrict__ packed,
+                                                                const uint32_t* __restrict__ kstart,
+                                                                const int64_t* __restrict__ actual) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + uniform(static_cast<int>(threadIdx.x) / kWave);
+  if (i >= uniform64(*actual)) return;
+  const uint32_t s = uniform(inv[i]);
+  const uint32_t lane = lane_id();
+  const uint32_t pk = packed[s];  // used after the row loads are issued
+  const uint8_t* src = slot_row(a, s);
+  uint8_t* dst = a.y + i * a.row_bytes;
+  const int64_t n16 = a.row_bytes >> 4;
+  RowPiece<VEC> first;
+  if (VEC != 1) first.load(src, n16, 0, lane);
+  const uint32_t c = s / static_cast<uint32_t>(a.chunk);
+  const uint32_t gstart = kstart[pk >> 16];
+  const int32_t ses = a.session_ids ? a.session_ids[c] : static_cast<int32_t>(c);
+  const int32_t mb = a.micro_batch_ids ? a.micro_batch_ids[c] : 0;
+  if (lane == 0) {
+    a.token_ids[i] = static_cast<int32_t>(s);
+    a.offsets[i] = static_cast<int32_t>(static_cast<uint32_t>(i) - gstart);
+    a.session_out[i] = ses;
+    a.mb_out[i] = mb;
+    if (a.dyn_scale != nullptr) a.dyn_scale[i] = load_scale(slot_scale(a, s));
+  }
+  if (VEC != 1) {
+    first.store(dst, n16, 0, lane);
+    copy_row_rest<VEC>(src, dst, a.row_bytes, kWave * kPiece, lane);
+  } else {
+    copy_row_rest<VEC>(src, dst, a.row_bytes, 0, lane);
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 SortPass make_pass(int64_t n, int nb, int nbits, int shift) {
@@ -627,6 +766,7 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p, bool from_conte
   // slot counts (measured crossover with the rank / scan / gather path: ~8K slots)
   p->wg_order = !p->small && Y <= kWgMaxSlots && nb <= kWgMaxKeys;
   p->range_order = !p->small && !p->wg_order && ro_fits(Y, static_cast<uint64_t>(nb), kBatchingRangeMaxSlots);
+  p->place = !p->small && !p->wg_order && !p->range_order && p->pass.nt <= kPlaceMaxTiles;
   if (p->small) {
     p->ws_bytes = 0;
   } else if (p->wg_order || p->range_order) {
@@ -640,6 +780,7 @@ int plan_batching(const ffnwb_batching_desc* d, BatchingPlan* p, bool from_conte
     c.take<uint32_t>(static_cast<size_t>(nb) * p->pass.nt);           // histogram -> offsets
     c.take<uint32_t>(static_cast<size_t>(nb) + 1);                    // key starts
     c.take<uint32_t>(p->pass.nt);                                     // per-tile bad-id counts
+    if (p->place) c.take<uint32_t>(Y);                                // slot of every output row
     p->ws_bytes = c.off;
   }
   return FFNWB_OK;
@@ -766,6 +907,33 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
     hipLaunchKernelGGL((sort_rank_kernel<16, KeyBatching>), dim3(p.pass.nt), dim3(kRankThreads), lds, s, ks, p.Y, 0,
                        p.pass.nbits, nb, packed, hist, tile_err);
   if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+
+  if (p.place) {
+    uint32_t* inv = c.take<uint32_t>(p.Y);
+    const size_t plds = 2 * static_cast<size_t>(nb) * sizeof(uint32_t);
+    auto place = [&](auto bc) {
+      constexpr int B = decltype(bc)::value;
+      allow_large_lds(reinterpret_cast<const void*>(&batching_place_kernel<B>), plds);
+      hipLaunchKernelGGL(batching_place_kernel<B>, dim3(p.pass.nt), dim3(kWgThreads), plds, s, a,
+                         static_cast<const uint32_t*>(packed), static_cast<const uint32_t*>(hist),
+                         static_cast<const uint32_t*>(tile_err), nb, p.pass.nt, p.pass.tile_shift, inv, kstart,
+                         d->group_list, d->expert_num, d->actual_token_num, d->err_count);
+    };
+    if (p.pass.nt <= 16) place(std::integral_constant<int, 16>());
+    else if (p.pass.nt <= 32) place(std::integral_constant<int, 32>());
+    else place(std::integral_constant<int, 64>());
+    if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
+    const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
+    bool launched = false;
+    err = launch_vec(p.vec, [&](auto v) {
+      launched = launch_bound(batching_copy_out_kernel<decltype(v)::value>, dim3(blocks), dim3(256), 0, s,
+                              d->ev_gather_begin, d->ev_gather_end, a, static_cast<const uint32_t*>(inv),
+                              static_cast<const uint32_t*>(packed), static_cast<const uint32_t*>(kstart),
+                              static_cast<const int64_t*>(d->actual_token_num));
+    });
+    if (!launched) return FFNWB_ERR_RUNTIME;
+    return err == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+  }
 
   ScanTail tail{d->group_list, d->expert_num, d->actual_token_num, d->err_count, tile_err};
   const size_t scan_lds = scan_lds_bytes(nb);

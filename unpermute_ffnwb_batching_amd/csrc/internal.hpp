@@ -66,6 +66,7 @@ struct BatchingPlan {
   const uint8_t* scale_base = nullptr;
   int64_t scale_stride = 0;
   bool small = false;  // single fused workgroup
+  bool place = false;        // rank, then placement by tiles (no scan launch), then a copy in output order
   bool wg_order = false;     // slot order in one 1024-thread workgroup, then a row copy
   bool range_order = false;  // slot order in one range-partitioned launch, then a row copy
   SortPass pass;
