@@ -500,7 +500,7 @@ def main():
     # parity of the timed outputs and the CPU oracle baseline, on the host
     parity = None
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cases:
         from _gpu import oracle_batching, oracle_unpermute
         t_or = {}
         refs = {}
@@ -588,7 +588,7 @@ def main():
         next_rows["unpermute_padded_skip_zero_weight"] = measure_skip(args, stream, cases["unpermute_padded"])
     next_rows = next_rows or None
 
-    value = step_bytes / (ms * 1e-3) / 1e9
+    value = step_bytes / (ms * 1e-3) / 1e9 if step_bytes else 0.0
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "ms_per_step_without_timing_hooks": round(ms_nohook, 4),

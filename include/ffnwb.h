@@ -352,7 +352,9 @@ int moe_unpermute_noalloc(const moe_unpermute_desc* d, void* stream);
  *   sorted_indices[e*C + j] = the j-th token (ascending) routed to expert e, for j below
  *   min(C, the expert's token count); -1 for the rest.  Row i of permuted_tokens = token
  *   row sorted_indices[i], zero where that is -1.  Tokens past the capacity are dropped.
- * Rows are moved as bytes.  Supported: E <= 256 and ceil(T / 256) * E <= 16384.
+ * Rows are moved as bytes.  Supported: E <= 8192 and T * E < 2^31.  Up to 256 experts with
+ * ceil(T / 256) * E <= 16384 the order takes one launch after the map count; larger maps
+ * take a four-launch order through a [T][E] table in the workspace (4 * T * E bytes).
  * ------------------------------------------------------------------------------------------ */
 typedef struct moe_permute_desc {
   int32_t dtype;             /* element type of the rows: FFNWB_DT_FP16, _BF16, _FP32, or _INT8
@@ -360,7 +362,7 @@ typedef struct moe_permute_desc {
   int32_t padded_mode;       /* 0 = token-slot layout, 1 = expert-capacity layout */
   int64_t num_tokens;        /* T >= 1 */
   int64_t hidden;            /* H > 0 elements per row */
-  int64_t num_experts;       /* E in [1, 256] */
+  int64_t num_experts;       /* E in [1, 8192] */
   int64_t num_out_rows;      /* N >= 0 (see above) */
   int64_t capacity;          /* C >= 0, padded mode only */
   int64_t token_row_stride;  /* bytes between token rows; 0 = H * element size */

@@ -308,13 +308,22 @@ def test_permute_required_pointers(field):
 
 @pytest.mark.parametrize("over", [
     dict(dtype=9), dict(padded_mode=3), dict(num_tokens=0), dict(hidden=0), dict(num_experts=0),
-    dict(num_experts=257), dict(num_out_rows=100),                    # not a multiple of T
+    dict(num_experts=8193), dict(num_out_rows=100),                   # not a multiple of T
     dict(padded_mode=1, num_out_rows=100, capacity=20),               # not E * C
-    dict(num_experts=256, num_tokens=16385, num_out_rows=16385),      # histogram beyond LDS
+    dict(num_experts=8192, num_tokens=262144, num_out_rows=262144),   # T * E >= 2^31
     dict(token_row_stride=63), dict(capacity=-1),
 ])
 def test_permute_invalid_parameters(over):
     assert _pws(_permute_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_permute_wide_maps_take_the_table_order():
+    # more than 256 experts, or a tile histogram beyond one workgroup's LDS: the [T][E] table
+    for T, E in ((64, 257), (16385, 256), (65536, 128), (1024, 8192)):
+        st, n = _pws(_permute_desc(num_tokens=T, num_experts=E, num_out_rows=T * 2))
+        assert st == 0 and n >= 4 * T * E, (T, E)
+        st, n = _pws(_permute_desc(padded_mode=1, num_tokens=T, num_experts=E, num_out_rows=E * 3, capacity=3))
+        assert st == 0 and n >= 4 * T * E, (T, E)
 
 
 def test_permute_workspace():

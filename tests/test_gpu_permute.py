@@ -36,6 +36,13 @@ NONPAD = [
     (256, 1, 4, 16, synth.FP16, "uniform", 0, "all"),         # every token to all experts: rows dropped past N
     (77, 5, 256, 24, synth.BF16, "uniform", 0, None),         # E = 256
     (64, 3, 12, 8, synth.FP16, "uniform", 0, "none"),         # empty map: zero rows, -1 slots
+    # four-launch order through the [T][E] table (more than 256 experts, or large maps)
+    (4096, 8, 512, 64, synth.BF16, "uniform", 0, None),       # E = 512
+    (300, 70, 300, 24, synth.FP32, "skew", 0, "more"),        # E not a multiple of 4, topK = 70 > 64
+    (2000, 3, 1000, 16, synth.INT8, "uniform", 3, None),      # byte rows, strided tokens
+    (40, 300, 512, 8, synth.BF16, "uniform", 0, "all300"),    # 300 rows per token: the list is copied in two parts
+    (50, 200, 8192, 8, synth.FP16, "uniform", 0, None),       # the most experts
+    (9000, 2, 260, 32, synth.FP16, "skew", 0, "more"),        # 260 experts: rows dropped past N
 ]
 
 
@@ -50,6 +57,8 @@ def test_nonpadded(params):
         n_t = np.full(T, E)
     elif mode == "none":
         n_t = np.zeros(T, np.int64)
+    elif mode == "all300":
+        n_t = np.full(T, 300)
     case = synth.permute_case(700 + T + E, T=T, K=K, E=E, H=H, dtype=dt, route=route, row_pad=pad, n_t=n_t)
     print(f"permute non-padded {params}", flush=True)
     check_permute(case, run_permute(case))
@@ -65,6 +74,11 @@ PAD = [
     (300, 256, 30, 16, synth.BF16, 200),   # up to 200 experts per token: four 64-entry table chunks
     (150, 200, 64, 24, synth.FP16, 130),   # partial last table chunk (200 = 3*64 + 8)
     (90, 130, 20, 8, synth.INT8, 100),     # E not a multiple of 4 (byte map loads) with partial chunks
+    # four-launch order through the [T][E] table
+    (4096, 512, 64, 32, synth.BF16, 8),    # E = 512
+    (64, 512, 64, 8, synth.FP16, 300),     # 300 capacity rows per token: the list is copied in two parts
+    (3000, 1000, 7, 24, synth.FP32, 5),    # capacity overflow over 1000 experts
+    (5000, 301, 40, 13, synth.INT8, 4),    # E not a multiple of 4, byte rows
 ]
 
 
@@ -141,3 +155,58 @@ def test_padded_round_trip_is_count_times_x():
     x = permute_tokens(case).astype(np.float64)
     n_t = case["routing_map"].sum(axis=1).astype(np.float64)
     assert np.array_equal(back.cpu().numpy(), (x * n_t[:, None] + 0.0).astype(np.float32))
+
+
+def _permute_indices(rmap, N, padded, C=None):
+    """sorted_indices from library routines (torch.nonzero lists entries expert-major,
+    cumsum ranks a token's experts), independent of the oracle's loops."""
+    m = torch.from_numpy(rmap != 0)
+    T, E = m.shape
+    e_idx, t_idx = torch.nonzero(m.t(), as_tuple=True)       # expert-major entry order
+    out = torch.full((N,), -1, dtype=torch.int64)
+    if padded:
+        place = torch.cumsum(m.t().long(), dim=1) - 1           # rank of t within expert e
+        p = place[e_idx, t_idx]
+        keep = p < C
+        out[e_idx[keep] * C + p[keep]] = t_idx[keep]
+        return out.numpy()
+    K = N // T
+    row = torch.full((T, E), -1, dtype=torch.int64)
+    row[t_idx, e_idx] = torch.arange(e_idx.numel())
+    k = torch.cumsum(m.long(), dim=1) - 1                        # rank of e within token t
+    tt, ee = torch.nonzero(m, as_tuple=True)
+    kk = k[tt, ee]
+    r = row[tt, ee]
+    keep = kk < K
+    out[tt[keep] * K + kk[keep]] = torch.where(r[keep] < N, r[keep], torch.full_like(r[keep], -1))
+    return out.numpy()
+
+
+@pytest.mark.parametrize("T,E,padded", [(4096, 512, False), (65536, 128, False), (4096, 512, True),
+                                        (65536, 128, True)])
+def test_table_order_round_trip_is_count_times_x(T, E, padded):
+    # the four-launch order at E = 512 and at T = 65536 (256 tiles x 128 experts): the
+    # permute's indices against a construction from library routines, then permute ->
+    # unpermute gives every token's row once per expert it kept, exactly
+    H, K = 64, 4
+    rng = np.random.default_rng(905 + T + E)
+    n_t = rng.integers(0, K + 1, size=T)
+    rmap = np.zeros((T, E), np.int8)
+    for t in np.nonzero(n_t)[0]:
+        rmap[t, rng.choice(E, size=int(n_t[t]), replace=False)] = 1
+    x = synth._normal_elements(rng, (T, H), synth.FP32)
+    tokens = dev(x)
+    C = int(rmap.sum(axis=0).max()) - 1 if padded else 0   # one token dropped from the fullest expert
+    N = E * C if padded else T * K
+    call = F.PermuteCall(tokens, dev(rmap), padded_mode=padded, num_out_rows=N, capacity=C)
+    print(f"permute table order T={T} E={E} padded={padded}", flush=True)
+    call.run()
+    torch.cuda.synchronize()
+    sI = call.out["sorted_indices"].cpu().numpy()
+    assert np.array_equal(sI, _permute_indices(rmap, N, padded, C))
+    back = _gpu_unpermute(call.out["permuted_tokens"], call.out["sorted_indices"], synth.FP32, T, H, padded=padded)
+    if padded:
+        kept = np.bincount(sI[sI >= 0], minlength=T).astype(np.float64)
+    else:
+        kept = (sI.reshape(T, K) >= 0).sum(axis=1).astype(np.float64)
+    assert np.array_equal(back.cpu().numpy(), (x.astype(np.float64) * kept[:, None] + 0.0).astype(np.float32))

@@ -112,6 +112,7 @@ struct PermutePlan {
   int64_t T = 0, E = 0, N = 0, K = 0, ntiles = 0;
   int64_t row_bytes = 0, stride = 0;
   bool padded = false;
+  bool table = false;  // four-launch order through a [T][E] table (many experts or tiles)
   size_t ws_bytes = 0;
 };
 

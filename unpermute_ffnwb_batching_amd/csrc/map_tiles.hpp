@@ -39,6 +39,27 @@ __device__ __forceinline__ void mask_item_counts(const uint8_t* __restrict__ map
   }
 }
 
+// Maps whose tile histogram does not fit one workgroup's LDS: tiles of kMaskTile tokens,
+// thread e of a tile's workgroup walks column e of the tile, so within a column the
+// tile's entries are in token order and their rank is a running count.
+constexpr int kMaskTile = 32;
+
+// hist[tile*E + e] = number of non-zero map entries of column e in the tile.
+[[maybe_unused]] static __global__ __launch_bounds__(256) void mask_count_kernel(const uint8_t* __restrict__ map,
+                                                                                 int64_t T, int32_t E,
+                                                                                 uint32_t* __restrict__ hist) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    uint8_t m[kMaskTile];
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) m[i] = map[(t0 + i < T ? t0 + i : T - 1) * E + e];  // clamped: no branch
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) c += (t0 + i < T && m[i] != 0) ? 1u : 0u;
+    hist[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+  }
+}
+
 constexpr int kMaskRangeUnits = 8;                                // work-item columns per range
 constexpr int kMaskSplitThreads = kMaskGroups * kMaskRangeUnits;   // 128: one item per thread
 

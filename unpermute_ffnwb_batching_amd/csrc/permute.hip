@@ -27,6 +27,11 @@
 //      padded token row once per expert it is routed to: 121.7 us for the row moves at
 //      E=64, C=512, T=8192, H=5120 FP16 with 4 experts per token, against 77-84 us in
 //      token order.
+// Maps with more than kPermuteMaxExperts experts, or whose tile histogram does not fit
+// one workgroup's LDS, take four launches instead: mask_count_kernel (32-token tiles),
+// the histogram scan, permute_table_kernel (the row, or capacity row, of every (t, e) in
+// a [T][E] table), and permute_scatter_kernel reading its lists from that table, which
+// then also writes the non-padded sorted_indices.
 #include <stdio.h>
 
 #include "internal.hpp"
@@ -315,6 +320,56 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_order_kernel(const ui
     if (r >= filled) source_of[r] = -1;
 }
 
+// Fallback order (see the file comment), after mask_count_kernel and the histogram scan
+// over 32-token tiles: thread e of a tile's workgroup walks column e of the tile in token
+// order, so a running count from the tile's base gives each entry its place among the
+// column's entries:
+//   non-padded  row start[e] + (entries of column e in earlier tiles) + running count;
+//   padded      place j = (entries in earlier tiles) + running count: capacity row
+//               e*C + j while j < C, with sorted_indices[e*C + j] = t.
+// table[t*E + e] = that row (non-padded rows may lie past N: dropped later), or -1 for a
+// zero entry or a padded entry past the capacity.  Padded, every workgroup also takes a
+// share of the unused capacity: sorted_indices = -1.
+template <bool PADDED>
+__global__ __launch_bounds__(256) void permute_table_kernel(const uint8_t* __restrict__ map, int64_t T, int32_t E,
+                                                            Placement pl, int64_t C, int32_t* __restrict__ table,
+                                                            int32_t* __restrict__ sorted_indices) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMaskTile;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    uint32_t off = pl.tile_base(blockIdx.x, static_cast<uint32_t>(e));
+    const uint32_t first = pl.start[e];
+    uint8_t m[kMaskTile];
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) m[i] = map[min(t0 + i, T - 1) * E + e];  // clamped: no branch
+#pragma unroll
+    for (int i = 0; i < kMaskTile; ++i) {
+      const int64_t t = t0 + i;
+      if (t >= T) break;
+      int32_t v = -1;
+      if (m[i] != 0) {
+        if (PADDED) {
+          if (off < static_cast<uint64_t>(C)) {
+            v = static_cast<int32_t>(e * C + off);
+            sorted_indices[e * C + off] = static_cast<int32_t>(t);
+          }
+        } else {
+          v = static_cast<int32_t>(first + off);
+        }
+        ++off;
+      }
+      table[t * E + e] = v;
+    }
+  }
+  if (PADDED) {
+    const int64_t all = static_cast<int64_t>(E) * C;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < all;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+      const int64_t e = i / C;
+      if (i - e * C >= static_cast<int64_t>(pl.start[e + 1] - pl.start[e])) sorted_indices[i] = -1;
+    }
+  }
+}
+
 // Writes zeros over one row (one wavefront).
 template <int VEC>
 __device__ __forceinline__ void zero_row(uint8_t* __restrict__ dst, int64_t row_bytes, uint32_t lane) {
@@ -333,71 +388,94 @@ __device__ __forceinline__ void zero_row(uint8_t* __restrict__ dst, int64_t row_
   }
 }
 
-// Row moves.  Workgroups below token_blocks: one wavefront per token loads each 16 KiB
-// piece of the token's row once and stores it to every row its list names
-// (lists[t*K .. t*K+K), -1 = none; K = topK non-padded, E padded), with ordinary stores:
-// this kernel writes several times what it reads, and for such write-heavy traffic
-// ordinary stores measured 4% faster than non-temporal ones (242 vs 251 us at T=16384,
-// topK=8, H=4096 BF16).  The rest: one wavefront per 64 output rows handles the rows no
-// list names: source_of[r] = -1 (zeros) or -(t+2) (token t); rows with source_of[r] >= 0
-// are the token wavefronts'.
+// Row moves.  Workgroups below token_blocks: one wavefront per token reads its list
+// (lists[t*K .. t*K+K), -1 = none; K = topK non-padded, E padded or from the [T][E]
+// table) 64 entries at a time and gathers the rows in [0, N) it names into a per-wave LDS
+// list; then it loads each 16 KiB piece of the token's row once and stores it to every
+// listed row, with ordinary stores: this kernel writes several times what it reads, and
+// for such write-heavy traffic ordinary stores measured 4% faster than non-temporal ones
+// (242 vs 251 us at T=16384, topK=8, H=4096 BF16).  With topk > 0 the list is the
+// non-padded table, and the wavefront also writes the token's slots: sorted_out[t*topk +
+// k] = the row of its k-th listed entry (-1 past N, and for k past its entries).
+// The rest: one wavefront per 64 output rows handles the rows no list names:
+// source_of[r] = -1 (zeros) or -(t+2) (token t), or, without source_of, zeros for the
+// rows from *filled (the number of non-zero entries) up to N.
+constexpr int kDestCap = 256;  // listed rows a wavefront gathers before it copies
+
+template <int VEC>
+__device__ __forceinline__ void copy_to_rows(const uint8_t* __restrict__ src, int64_t row_bytes,
+                                             const int32_t* rows, uint32_t nd, uint8_t* __restrict__ out,
+                                             uint32_t lane) {
+  if (VEC == 1) {
+    for (uint32_t j = 0; j < nd; ++j) copy_row<1>(src, out + static_cast<int64_t>(rows[j]) * row_bytes, row_bytes, lane);
+    return;
+  }
+  const int64_t n16 = row_bytes >> 4;
+  for (int64_t b = 0; b < n16; b += kWave * kPiece) {
+    RowPiece<VEC> piece;
+    piece.load(src, n16, b, lane);
+    for (uint32_t j = 0; j < nd; ++j) piece.store_cached(out + static_cast<int64_t>(rows[j]) * row_bytes, n16, b, lane);
+  }
+  if (VEC == 4) {
+    const int64_t tail = (row_bytes & 15) >> 2;
+    uint32_t v = 0;
+    if (lane < tail) v = reinterpret_cast<const uint32_t*>(src + n16 * 16)[lane];
+    for (uint32_t j = 0; j < nd; ++j)
+      if (lane < tail) reinterpret_cast<uint32_t*>(out + static_cast<int64_t>(rows[j]) * row_bytes + n16 * 16)[lane] = v;
+  }
+}
+
 template <int VEC>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
                                                               int64_t row_bytes,
                                                               const int32_t* __restrict__ lists, int64_t T,
-                                                              int32_t K, const int32_t* __restrict__ source_of,
-                                                              int64_t N, unsigned token_blocks,
-                                                              uint8_t* __restrict__ out) {
+                                                              int32_t K, int32_t topk,
+                                                              int32_t* __restrict__ sorted_out,
+                                                              const int32_t* __restrict__ source_of,
+                                                              const uint32_t* __restrict__ filled, int64_t N,
+                                                              unsigned token_blocks, uint8_t* __restrict__ out) {
+  __shared__ int32_t dests[4][kDestCap];
   const uint32_t lane = lane_id();
   const int wv = uniform(static_cast<int>(threadIdx.x) / kWave);
   if (blockIdx.x < token_blocks) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
     if (t >= T) return;
     const uint8_t* src = tokens + t * stride;
-    const int64_t n16 = row_bytes >> 4;
-    for (int k0 = 0; k0 < K; k0 += kWave) {
-      const int32_t d = (k0 + static_cast<int>(lane) < K) ? lists[t * K + k0 + lane] : -1;
-      const uint64_t m = wave_ballot(d >= 0);
-      if (m == 0) continue;
-      if (VEC == 1) {
-        uint64_t mm = m;
-        while (mm != 0) {
-          const int l = static_cast<int>(__builtin_ctzll(mm));
-          mm &= mm - 1;
-          const int64_t r = __builtin_amdgcn_readlane(d, l);
-          copy_row<1>(src, out + r * row_bytes, row_bytes, lane);
-        }
-        continue;
+    int32_t* dl = dests[wv];
+    uint32_t nd = 0, k0 = 0;
+    for (int c0 = 0; c0 < K; c0 += kWave) {
+      const int32_t d = (c0 + static_cast<int>(lane) < K) ? lists[t * K + c0 + lane] : -1;
+      if (topk > 0) {
+        const uint64_t nz = wave_ballot(d != -1);
+        const uint32_t k = k0 + count_below(nz);
+        if (d != -1 && k < static_cast<uint32_t>(topk))
+          sorted_out[t * topk + k] = (d >= 0 && d < N) ? d : -1;
+        k0 += static_cast<uint32_t>(__popcll(nz));
       }
-      for (int64_t b = 0; b < n16; b += kWave * kPiece) {
-        RowPiece<VEC> piece;
-        piece.load(src, n16, b, lane);
-        uint64_t mm = m;
-        while (mm != 0) {
-          const int l = static_cast<int>(__builtin_ctzll(mm));
-          mm &= mm - 1;
-          const int64_t r = __builtin_amdgcn_readlane(d, l);
-          piece.store_cached(out + r * row_bytes, n16, b, lane);
-        }
+      const bool ok = d >= 0 && d < N;
+      const uint64_t m = wave_ballot(ok);
+      if (ok) dl[nd + count_below(m)] = d;
+      nd += static_cast<uint32_t>(__popcll(m));
+      if (nd > kDestCap - kWave) {  // the next chunk might not fit: copy now
+        wave_lds_sync();
+        copy_to_rows<VEC>(src, row_bytes, dl, nd, out, lane);
+        wave_lds_sync();
+        nd = 0;
       }
-      if (VEC == 4) {
-        const int64_t tail = (row_bytes & 15) >> 2;
-        uint32_t v = 0;
-        if (lane < tail) v = reinterpret_cast<const uint32_t*>(src + n16 * 16)[lane];
-        uint64_t mm = m;
-        while (mm != 0) {
-          const int l = static_cast<int>(__builtin_ctzll(mm));
-          mm &= mm - 1;
-          const int64_t r = __builtin_amdgcn_readlane(d, l);
-          if (lane < tail) reinterpret_cast<uint32_t*>(out + r * row_bytes + n16 * 16)[lane] = v;
-        }
-      }
+    }
+    if (topk > 0)
+      for (uint32_t q = k0 + lane; q < static_cast<uint32_t>(topk); q += kWave) sorted_out[t * topk + q] = -1;
+    if (nd > 0) {
+      wave_lds_sync();
+      copy_to_rows<VEC>(src, row_bytes, dl, nd, out, lane);
     }
     return;
   }
   const int64_t r0 = (static_cast<int64_t>(blockIdx.x - token_blocks) * 4 + wv) * kWave;
   const int64_t r = r0 + lane;
-  const int32_t v = (r < N) ? source_of[r] : 0;
+  int32_t v = 0;
+  if (source_of != nullptr) v = (r < N) ? source_of[r] : 0;
+  else v = (r < N && r >= static_cast<int64_t>(*filled)) ? -1 : 0;
   uint64_t m = wave_ballot(r < N && v < 0);
   while (m != 0) {
     const int l = static_cast<int>(__builtin_ctzll(m));
@@ -427,11 +505,12 @@ int plan_permute(const moe_permute_desc* d, PermutePlan* p) {
   if (elt == 0) return FFNWB_ERR_PARAM_INVALID;
   if (d->padded_mode != 0 && d->padded_mode != 1) return FFNWB_ERR_PARAM_INVALID;
   const int64_t T = d->num_tokens, H = d->hidden, E = d->num_experts, N = d->num_out_rows;
-  if (T < 1 || H < 1 || E < 1 || E > kPermuteMaxExperts || N < 0 || d->capacity < 0) return FFNWB_ERR_PARAM_INVALID;
+  if (T < 1 || H < 1 || E < 1 || E > kMaxExperts || N < 0 || d->capacity < 0) return FFNWB_ERR_PARAM_INVALID;
   const int64_t lim = (int64_t{1} << 31) - 1;
   if (T > lim / E || N > lim || H > (int64_t{1} << 30)) return FFNWB_ERR_PARAM_INVALID;
   const int64_t ntiles = (T + kMaskRows - 1) / kMaskRows;
-  if (ntiles * E > kMaskLdsHist) return FFNWB_ERR_PARAM_INVALID;
+  // the one-launch order holds the tile histogram and a byte per (row, expert) of a tile in LDS
+  p->table = E > kPermuteMaxExperts || ntiles * E > kMaskLdsHist;
   p->padded = d->padded_mode == 1;
   if (p->padded) {
     if (N != E * d->capacity) return FFNWB_ERR_PARAM_INVALID;
@@ -450,22 +529,75 @@ int plan_permute(const moe_permute_desc* d, PermutePlan* p) {
   p->N = N;
   p->ntiles = ntiles;
   Carve c;
-  c.take<uint32_t>(static_cast<size_t>(ntiles * E));       // tile histogram
-  if (!p->padded) c.take<int32_t>(static_cast<size_t>(N));  // source token of every row
-  else c.take<int32_t>(static_cast<size_t>(T * E));         // capacity row of every entry
+  if (p->table) {
+    const int64_t nt32 = (T + kMaskTile - 1) / kMaskTile;
+    c.take<uint32_t>(static_cast<size_t>(nt32 * E));       // 32-token tile histogram -> offsets
+    c.take<uint32_t>(static_cast<size_t>(E) + 1);          // column starts
+    c.take<int32_t>(static_cast<size_t>(T * E));           // (capacity) row of every entry
+  } else {
+    c.take<uint32_t>(static_cast<size_t>(ntiles * E));       // tile histogram
+    if (!p->padded) c.take<int32_t>(static_cast<size_t>(N));  // source token of every row
+    else c.take<int32_t>(static_cast<size_t>(T * E));         // capacity row of every entry
+  }
   p->ws_bytes = c.off;
   return FFNWB_OK;
+}
+
+template <typename... Args>
+static bool launch_scatter(int vec, dim3 grid, hipStream_t s, void* evb, void* eve, Args... args) {
+  if (vec == 16) return launch_bound(permute_scatter_kernel<16>, grid, dim3(256), 0, s, evb, eve, args...);
+  if (vec == 4) return launch_bound(permute_scatter_kernel<4>, grid, dim3(256), 0, s, evb, eve, args...);
+  return launch_bound(permute_scatter_kernel<1>, grid, dim3(256), 0, s, evb, eve, args...);
 }
 
 int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hipStream_t s) {
   if (p.N == 0) return FFNWB_OK;
   Carve c;
   c.base = static_cast<char*>(ws);
+  const uint8_t* map = d->routing_map;
+  const int32_t E = static_cast<int32_t>(p.E);
+  const int vec = vec_class(reinterpret_cast<uintptr_t>(d->tokens), reinterpret_cast<uintptr_t>(d->permuted_tokens),
+                            p.stride, p.row_bytes, p.row_bytes);
+  const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
+  uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
+  // the optional hooks are bound to the row-copy launch
+  void* evb = d->ev_copy_begin;
+  void* eve = d->ev_copy_end;
+  const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
+  const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
+  if (p.table) {
+    const int nt32 = static_cast<int>((p.T + kMaskTile - 1) / kMaskTile);
+    uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(nt32) * E);
+    uint32_t* start = c.take<uint32_t>(static_cast<size_t>(E) + 1);
+    int32_t* table = c.take<int32_t>(static_cast<size_t>(p.T * p.E));
+    const int th = static_cast<int>(E >= 256 ? 256 : (E + 63) / 64 * 64);
+    hipLaunchKernelGGL(mask_count_kernel, dim3(nt32), dim3(th), 0, s, map, p.T, E, hist);
+    ScanTail none{nullptr, 0, nullptr, nullptr, nullptr};
+    const size_t lds = scan_lds_bytes(E);
+    allow_large_lds(reinterpret_cast<const void*>(&scan_hist_kernel), lds);
+    hipLaunchKernelGGL(scan_hist_kernel, dim3(1), dim3(kScanThreads), lds, s, hist, static_cast<int>(E), nt32, start,
+                       static_cast<uint32_t*>(nullptr), none);
+    const Placement pl{nullptr, hist, start, static_cast<int>(E), 0};
+    if (p.padded)
+      hipLaunchKernelGGL(permute_table_kernel<true>, dim3(nt32), dim3(th), 0, s, map, p.T, E, pl, d->capacity, table,
+                         d->sorted_indices);
+    else
+      hipLaunchKernelGGL(permute_table_kernel<false>, dim3(nt32), dim3(th), 0, s, map, p.T, E, pl, d->capacity, table,
+                         d->sorted_indices);
+    if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
+    // padded: rows whose sorted_indices entry is -1 are zero; non-padded: rows from the
+    // number of non-zero entries (start[E]) on
+    const bool ok = launch_scatter(vec, dim3(tb + rb), s, evb, eve, tok, p.stride, p.row_bytes,
+                                   static_cast<const int32_t*>(table), p.T, E,
+                                   static_cast<int32_t>(p.padded ? 0 : p.K), d->sorted_indices,
+                                   static_cast<const int32_t*>(p.padded ? d->sorted_indices : nullptr),
+                                   static_cast<const uint32_t*>(start + E), p.N, tb, out);
+    if (!ok) return FFNWB_ERR_RUNTIME;
+    return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
+  }
   uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(p.ntiles * p.E));
   int32_t* source_of = p.padded ? d->sorted_indices : c.take<int32_t>(static_cast<size_t>(p.N));
   int32_t* dest = p.padded ? c.take<int32_t>(static_cast<size_t>(p.T * p.E)) : nullptr;
-  const uint8_t* map = d->routing_map;
-  const int32_t E = static_cast<int32_t>(p.E);
   const int nt = static_cast<int>(p.ntiles);
   const bool wide = E % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0;
   const size_t lds = permute_order_lds_bytes(nt, E, p.padded);
@@ -486,30 +618,13 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
     else go(std::integral_constant<int, 1>(), std::false_type());
   }
   if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
-  const int vec = vec_class(reinterpret_cast<uintptr_t>(d->tokens), reinterpret_cast<uintptr_t>(d->permuted_tokens),
-                            p.stride, p.row_bytes, p.row_bytes);
-  const uint8_t* tok = static_cast<const uint8_t*>(d->tokens);
-  uint8_t* out = static_cast<uint8_t*>(d->permuted_tokens);
-  // the optional hooks are bound to the row-copy launch
-  void* evb = d->ev_copy_begin;
-  void* eve = d->ev_copy_end;
   // token rows to their rows: non-padded through the topK slots (rows past them through
   // source_of), padded through the [T][E] table (zero rows are sorted_indices' -1 entries)
-  const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
-  const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
   const int32_t K = static_cast<int32_t>(p.padded ? p.E : p.K);
   const int32_t* lists = p.padded ? dest : d->sorted_indices;
-  const int32_t* src = source_of;
-  bool ok;
-  if (vec == 16)
-    ok = launch_bound(permute_scatter_kernel<16>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
-  else if (vec == 4)
-    ok = launch_bound(permute_scatter_kernel<4>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
-  else
-    ok = launch_bound(permute_scatter_kernel<1>, dim3(tb + rb), dim3(256), 0, s, evb, eve, tok, p.stride,
-                      p.row_bytes, lists, p.T, K, src, p.N, tb, out);
+  const bool ok = launch_scatter(vec, dim3(tb + rb), s, evb, eve, tok, p.stride, p.row_bytes, lists, p.T, K,
+                                 int32_t{0}, static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(source_of),
+                                 static_cast<const uint32_t*>(nullptr), p.N, tb, out);
   if (!ok) return FFNWB_ERR_RUNTIME;
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }
