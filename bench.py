@@ -33,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# row bytes of each workload (the unit its row mover copies)
+ROW_BYTES = {"batching_bf16": 7168 * 2, "batching_int8": 7168, "unpermute_nonpadded": 4096 * 2,
+             "unpermute_padded": 5120 * 2}
 METRIC = "effective HBM GB/s (and % of peak) for batching and unpermute; rows/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "unpermute_reduce_nonpadded_bf16_T16384_topk8_H4096.traffic.txt")
 REDUCE_SOURCES = ["unpermute_ffnwb_batching_amd/csrc/reduce_kernels.hpp",
@@ -87,6 +90,39 @@ def warm_ms(run, stream, iters):
     e.record(stream)
     torch.cuda.synchronize()
     return b.elapsed_time(e) / iters
+
+
+PROBE_LIB = os.path.join(ROOT, "unpermute_ffnwb_batching_amd", "_lib", "libffnwb_probe.so")
+_PROBE = []
+
+
+def probe_copy_gbps(nbytes, row_bytes, stream, iters, shuffled=False):
+    """The library's row-mover access pattern as a plain copy (one wavefront per row,
+    16-byte non-temporal loads and stores; rows in a random order when shuffled) moving
+    nbytes (reads plus writes) in rows of row_bytes, flushed like the calls: the
+    achievable rate for that byte count and pattern on this GPU."""
+    import ctypes
+    import torch
+    if not _PROBE:
+        lib = ctypes.CDLL(PROBE_LIB)
+        lib.ffnwb_probe_copy_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        lib.ffnwb_probe_copy_rows.restype = ctypes.c_int
+        _PROBE.append(lib)
+    lib = _PROBE[0]
+    nrows = max(int(nbytes) // (2 * row_bytes), 1)
+    src = torch.empty(nrows * row_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    order = torch.randperm(nrows, dtype=torch.int32, device="cuda") if shuffled else None
+    optr = ctypes.c_void_p(order.data_ptr()) if order is not None else None
+
+    def run(st):
+        if lib.ffnwb_probe_copy_rows(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), row_bytes,
+                                     nrows, optr, ctypes.c_void_p(st.cuda_stream)) != 0:
+            raise RuntimeError("probe copy rejected")
+    ts = flushed_times(run, stream, iters)
+    del src, dst, order
+    return round(2 * nrows * row_bytes / float(np.median(ts)) / 1e6, 1)
 
 
 def copy_gbps(nbytes, stream, iters):
@@ -495,7 +531,10 @@ def main():
                          "pct_hbm_peak": round(100 * alg[n] / med / 1e6 / HBM_PEAK_GBS, 1),
                          "rows_per_s": round(rows[n] / med * 1e3, 1),
                          "us_warm": round(warm * 1e3, 2), "GBps_warm": round(alg[n] / warm / 1e6, 1),
-                         "copy_same_bytes_GBps": copy_gbps(alg[n], stream, 20)}
+                         "copy_same_bytes_GBps": copy_gbps(alg[n], stream, 20),
+                         "achievable_copy_GBps": probe_copy_gbps(alg[n], ROW_BYTES[n], stream, 20),
+                         "achievable_copy_shuffled_rows_GBps": probe_copy_gbps(alg[n], ROW_BYTES[n], stream, 20,
+                                                                               shuffled=True)}
 
     # parity of the timed outputs and the CPU oracle baseline, on the host
     parity = None
@@ -539,11 +578,29 @@ def main():
         act1 = int(call1.out["actual_token_num"].item())
         ts = flushed_times(call1.run, stream, args.detail_iters)
         warm = warm_ms(call1.run, stream, 100)
+        # device time per call without host submission: 100 calls captured in one graph
+        gstream = torch.cuda.Stream()
+        gstream.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            with torch.cuda.graph(g, stream=gstream):
+                for _ in range(100):
+                    call1.run(gstream)
+        stream.wait_stream(gstream)
+        g.replay()
+        torch.cuda.synchronize()
+        gb, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gb.record(stream)
+        for _ in range(5):
+            g.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        graph_us = gb.elapsed_time(ge) / 500 * 1e3
         latency = {"batching_tiny": {
             "shape": "A=2 BS=8 K+1=3 (Y=48) H=128 fp16, 16 experts, 5 slots masked",
             "us_median": round(float(np.median(ts)) * 1e3, 2), "us_p10": round(float(np.percentile(ts, 10)) * 1e3, 2),
             "us_p90": round(float(np.percentile(ts, 90)) * 1e3, 2), "iters": args.detail_iters,
-            "us_warm": round(warm * 1e3, 2), "rows": act1,
+            "us_warm": round(warm * 1e3, 2), "us_per_call_in_graph": round(graph_us, 2), "rows": act1,
             "rows_per_s": round(act1 / float(np.median(ts)) * 1e3, 1)}}
         if not args.no_cpu_baseline:
             from _gpu import oracle_batching

@@ -421,7 +421,7 @@ typedef struct moe_update_expert_desc {
   int32_t scale_dtype;      /* FFNWB_DT_FP16, _BF16 or _FP32; ignored without scales */
   int32_t reserved0;        /* must be 0 */
 
-  /* Inputs (dense, row-major). */
+  /* Inputs (row-major; see the strides below). */
   const void* expert_ids;          /* [BS, K] of id_dtype */
   const int32_t* eplb_table;       /* [E, F] */
   const void* expert_scales;       /* [BS, K] of scale_dtype, or NULL */
@@ -432,12 +432,25 @@ typedef struct moe_update_expert_desc {
   void* balanced_expert_ids;       /* [BS, K] of id_dtype, required */
   uint8_t* balanced_active_mask;   /* [BS, K] bool; required with scales, ignored without */
   int32_t* err_count;              /* [1] or NULL */
+
+  /* Layouts (the parameter table allows non-contiguous tensors): strides in ELEMENTS, 0 =
+     dense.  A 2-D tensor's elements along K (or F) are adjacent; its rows are the given
+     stride apart, at least the row length.  The 1-D threshold and mask take an element
+     stride >= 1. */
+  int64_t expert_ids_stride;       /* between tokens of expert_ids (0 = K) */
+  int64_t eplb_table_stride;       /* between experts of eplb_table (0 = F) */
+  int64_t expert_scales_stride;    /* between tokens of expert_scales (0 = K) */
+  int64_t threshold_stride;        /* between entries of pruning_threshold (0 = 1) */
+  int64_t active_mask_stride;      /* between tokens of active_mask (0 = 1) */
+  int64_t out_ids_stride;          /* between tokens of balanced_expert_ids (0 = K) */
+  int64_t out_mask_stride;         /* between tokens of balanced_active_mask (0 = K) */
 } moe_update_expert_desc;
 
 /* Validates *d and returns the workspace size (0) (host only).  Errors:
    FFNWB_ERR_PARAM_NULLPTR (d, ws_bytes or a required pointer NULL),
    FFNWB_ERR_PARAM_INVALID (a range above violated, dtype codes, scales given without a
-   threshold or the other way round, active_mask without scales, reserved0 != 0). */
+   threshold or the other way round, active_mask without scales, reserved0 != 0, a
+   negative stride or a row stride below its row length). */
 int moe_update_expert_workspace_size(const moe_update_expert_desc* d, size_t* ws_bytes);
 
 /* Validates again, then enqueues the update on `stream` (one launch). */

@@ -399,10 +399,18 @@ def test_update_expert_required_pointers(field):
     dict(k=8, moe_expert_num=7), dict(world_size=1), dict(world_size=769), dict(local_rank_id=-1),
     dict(local_rank_id=64), dict(table_cols=1), dict(table_cols=66), dict(balance_mode=2), dict(id_dtype=3),
     dict(id_dtype=0), dict(scale_dtype=4), dict(reserved0=1), dict(pruning_threshold=None),
-    dict(expert_scales=None),
+    dict(expert_scales=None), dict(expert_ids_stride=-1), dict(expert_ids_stride=1),      # below the row
+    dict(eplb_table_stride=2), dict(expert_scales_stride=3), dict(out_ids_stride=1), dict(out_mask_stride=5),
+    dict(threshold_stride=-2), dict(active_mask_stride=-1), dict(expert_ids_stride=(1 << 20) + 1),
 ])
 def test_update_expert_invalid_parameters(over):
     assert _uews(_ue_desc(**over))[0] == F.FFNWB_ERR_PARAM_INVALID
+
+
+def test_update_expert_strides_accepted():
+    d = _ue_desc(expert_ids_stride=100, eplb_table_stride=66, expert_scales_stride=9, threshold_stride=4,
+                 active_mask_stride=3, out_ids_stride=8, out_mask_stride=1 << 20)
+    assert _uews(d)[0] == 0
 
 
 def test_update_expert_active_mask_needs_scales():

@@ -121,3 +121,17 @@ def test_ctx_rejects_short_context_and_bad_outputs():
         F.BatchingCtxCall(torch.zeros(1000, dtype=torch.uint8), **kw)
     with pytest.raises(ValueError):
         F.BatchingCtxCall(ctx, out={"ctx_status": torch.zeros(2, dtype=i32)}, **kw)
+
+
+def test_update_expert_accepts_row_strided_views_and_rejects_bad_layouts():
+    ids = torch.zeros(8, 6, dtype=i32)[:, :4]
+    table = torch.ones(16, 5, dtype=i32)[:, :3]
+    c = F.UpdateExpertCall(ids, table, local_rank_id=0, world_size=2)
+    assert c.desc.expert_ids_stride == 6 and c.desc.eplb_table_stride == 5
+    with pytest.raises(ValueError):
+        F.UpdateExpertCall(torch.zeros(8, 8, dtype=i32)[:, ::2], table, local_rank_id=0, world_size=2)
+    with pytest.raises(ValueError):
+        F.UpdateExpertCall(ids, torch.ones(16, 3, dtype=i64), local_rank_id=0, world_size=2)
+    with pytest.raises(ValueError):
+        F.UpdateExpertCall(ids, table, local_rank_id=0, world_size=2, expert_scales=torch.zeros(8, 4),
+                           pruning_threshold=torch.zeros(5))

@@ -70,3 +70,46 @@ def test_repeat_is_bit_identical():
     for k in a:
         assert torch.equal(a[k].view(torch.uint8), call.out[k].view(torch.uint8)), k
     check_update_expert(c, call)
+
+
+def test_strided_views_of_every_input_and_output():
+    # the parameter table allows non-contiguous tensors: every input and output a view
+    # into a wider buffer (row strides for the 2-D tensors, an element stride for the
+    # threshold and the mask), against the oracle on the same values
+    import unpermute_ffnwb_batching_amd as F
+    from _gpu import dev, oracle_update_expert, to_torch_elems
+    for mode, idt, sdt in ((0, np.int32, synth.BF16), (1, np.int64, synth.FP32)):
+        c = synth.update_expert_case(7 + mode, 200, 6, 48, 16, 5, F=9, local_rank_id=11, balance_mode=mode,
+                                     id_dtype=idt, scale_dtype=sdt, n_active=150, n_bad_ids=5)
+        BS, K = c["expert_ids"].shape
+        E, Fc = c["eplb_table"].shape
+        ids_w = np.full((BS, K + 5), -7, dtype=idt)
+        ids_w[:, 2:2 + K] = c["expert_ids"]
+        tab_w = np.full((E, Fc + 3), 99999, np.int32)
+        tab_w[:, :Fc] = c["eplb_table"]
+        sc = to_torch_elems(c["expert_scales"], sdt)
+        sc_w = torch.zeros((BS, K + 2), dtype=sc.dtype, device="cuda")
+        sc_w[:, 1:1 + K] = sc
+        thr_w = torch.full((3 * K,), 1e30, dtype=torch.float32, device="cuda")
+        thr_w[::3] = dev(c["pruning_threshold"])
+        act_w = torch.zeros((2 * BS,), dtype=torch.bool, device="cuda")
+        act_w[::2] = dev(c["active_mask"])
+        out_ids_w = torch.full((BS, K + 4), -5, dtype=torch.int32 if idt == np.int32 else torch.int64, device="cuda")
+        out_mask_w = torch.full((BS, 2 * K), 7, dtype=torch.uint8, device="cuda")
+        out = {"balanced_expert_ids": out_ids_w[:, 3:3 + K], "balanced_active_mask": out_mask_w[:, 1:1 + K].view(torch.bool),
+               "err_count": torch.zeros(1, dtype=torch.int32, device="cuda")}
+        call = F.UpdateExpertCall(dev(ids_w)[:, 2:2 + K], dev(tab_w)[:, :Fc], local_rank_id=c["local_rank_id"],
+                                  world_size=c["world_size"], balance_mode=mode, expert_scales=sc_w[:, 1:1 + K],
+                                  pruning_threshold=thr_w[::3], active_mask=act_w[::2], out=out)
+        print(f"update expert, strided views, mode {mode}", flush=True)
+        call.run()
+        torch.cuda.synchronize()
+        ref = oracle_update_expert(c)
+        assert np.array_equal(out_ids_w[:, 3:3 + K].cpu().numpy(), ref["balanced_expert_ids"])
+        assert np.array_equal(out_mask_w[:, 1:1 + K].cpu().numpy(), ref["balanced_active_mask"].astype(np.uint8))
+        assert int(out["err_count"][0]) == ref["err_count"]
+        # the bytes around the views stay untouched
+        ow = out_ids_w.cpu().numpy()
+        assert (ow[:, :3] == -5).all() and (ow[:, 3 + K:] == -5).all()
+        om = out_mask_w.cpu().numpy()
+        assert (om[:, :1] == 7).all() and (om[:, 1 + K:] == 7).all()

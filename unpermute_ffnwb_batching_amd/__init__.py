@@ -173,6 +173,14 @@ def _check_numel(t, name, device, dtypes, numel):
     _req(t.numel() == numel, f"{name} has {t.numel()} elements, expected {numel}")
 
 
+def _check_rows(t, name, device, dtypes):
+    """A 2-D tensor whose elements along the last dimension are adjacent and whose rows
+    do not overlap (any row stride at least the row length)."""
+    _check_tensor(t, name, device, dtypes, contiguous=False)
+    _req(t.dim() == 2 and (t.shape[1] <= 1 or t.stride(1) == 1) and (t.shape[0] <= 1 or t.stride(0) >= t.shape[1]),
+         f"{name} must be 2-D with adjacent elements in each row (a row stride of at least the row length)")
+
+
 def _span_bytes(t):
     """Bytes from t's first element to just past its last (0 for an empty tensor)."""
     if t.numel() == 0:
@@ -682,15 +690,39 @@ def moe_update_expert_workspace_size(desc):
 class UpdateExpertCall:
     """A prepared moe_update_expert call.  ``expert_ids`` [BS, K] int32 / int64,
     ``eplb_table`` [E, F] int32, optional ``expert_scales`` [BS, K] (float16, bfloat16
-    or float32) with ``pruning_threshold`` [K] float32, and optional ``active_mask`` [BS]
-    bool, all dense device tensors."""
+    or float32) with ``pruning_threshold`` [K] or [1, K] float32, and optional
+    ``active_mask`` [BS] bool.  Any of them, and any output passed in ``out``, may be a
+    strided view, as long as a 2-D tensor's elements along K (or F) are adjacent."""
 
     def __init__(self, expert_ids, eplb_table, *, local_rank_id, world_size, balance_mode=0, expert_scales=None,
                  pruning_threshold=None, active_mask=None, out=None, with_err_count=True):
-        BS, K = expert_ids.shape
-        E, Fc = eplb_table.shape
+        _req(isinstance(expert_ids, torch.Tensor) and expert_ids.dim() == 2, "expert_ids must be [BS, K]")
         dev = expert_ids.device
+        BS, K = expert_ids.shape
+        _check_rows(expert_ids, "expert_ids", dev, tuple(_ID_CODE))
+        _req(isinstance(eplb_table, torch.Tensor) and eplb_table.dim() == 2, "eplb_table must be [E, F]")
+        _check_rows(eplb_table, "eplb_table", dev, _I32)
+        E, Fc = eplb_table.shape
+        if expert_scales is not None:
+            _req(tuple(expert_scales.shape) == (BS, K), f"expert_scales must be [{BS}, {K}]")
+            _check_rows(expert_scales, "expert_scales", dev, tuple(_FLOAT_CODE))
+            _req(pruning_threshold is not None, "expert_scales need pruning_threshold")
+            _req(pruning_threshold.numel() == K and pruning_threshold.shape[-1] == K,
+                 f"pruning_threshold must be [{K}] or [1, {K}]")
+            _check_tensor(pruning_threshold, "pruning_threshold", dev, (torch.float32,), contiguous=False)
+            if active_mask is not None:
+                _req(tuple(active_mask.shape) == (BS,), f"active_mask must be [{BS}]")
+                _check_tensor(active_mask, "active_mask", dev, _BYTES, contiguous=False)
         out = dict(out or {})
+        want = {"balanced_expert_ids": ((BS, K), (expert_ids.dtype,)), "balanced_active_mask": ((BS, K), _BYTES),
+                "err_count": ((1,), _I32)}
+        for k, t in out.items():
+            _req(k in want, f"unknown output {k!r}")
+            if k == "err_count":
+                _check_tensor(t, "out['err_count']", dev, _I32, (1,))
+            else:
+                _req(tuple(t.shape) == want[k][0], f"out[{k!r}] must be {want[k][0]}")
+                _check_rows(t, f"out[{k!r}]", dev, want[k][1])
         if "balanced_expert_ids" not in out:
             out["balanced_expert_ids"] = torch.empty((BS, K), dtype=expert_ids.dtype, device=dev)
         if expert_scales is not None and "balanced_active_mask" not in out:
@@ -699,6 +731,7 @@ class UpdateExpertCall:
             out["err_count"] = torch.empty(1, dtype=torch.int32, device=dev)
         self.out = out
         self._keep = [expert_ids, eplb_table, expert_scales, pruning_threshold, active_mask]
+        self._alloc_stream = _alloc_stream(dev)
         d = UpdateExpertDesc()
         d.bs, d.k, d.moe_expert_num, d.table_cols = BS, K, E, Fc
         d.local_rank_id, d.world_size, d.balance_mode = int(local_rank_id), int(world_size), int(balance_mode)
@@ -712,6 +745,19 @@ class UpdateExpertCall:
         d.balanced_expert_ids = _ptr(out["balanced_expert_ids"])
         d.balanced_active_mask = _ptr(out.get("balanced_active_mask"))
         d.err_count = _ptr(out.get("err_count"))
+        # strides in elements; 0 (dense) where a dimension of size 1 leaves torch's stride free
+        def rs(t):
+            return t.stride(0) if t.shape[0] > 1 else 0
+        d.expert_ids_stride = rs(expert_ids)
+        d.eplb_table_stride = rs(eplb_table)
+        if expert_scales is not None:
+            d.expert_scales_stride = rs(expert_scales)
+            d.threshold_stride = pruning_threshold.stride(-1) if K > 1 else 0
+            if active_mask is not None:
+                d.active_mask_stride = active_mask.stride(0) if BS > 1 else 0
+        d.out_ids_stride = rs(out["balanced_expert_ids"])
+        if "balanced_active_mask" in out:
+            d.out_mask_stride = rs(out["balanced_active_mask"])
         self.desc = d
         moe_update_expert_workspace_size(d)   # validates
 
@@ -719,6 +765,7 @@ class UpdateExpertCall:
         st = lib().moe_update_expert(ctypes.byref(self.desc), None, ctypes.c_size_t(0), _stream_handle(stream))
         if st != FFNWB_OK:
             raise FfnwbError(st, "moe_update_expert")
+        _record_on(list(self.out.values()), stream, self._alloc_stream)
         return self.out
 
 

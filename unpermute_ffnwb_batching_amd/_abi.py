@@ -91,4 +91,7 @@ class UpdateExpertDesc(ctypes.Structure):
         ("expert_ids", _vp), ("eplb_table", _vp), ("expert_scales", _vp), ("pruning_threshold", _vp),
         ("active_mask", _vp),
         ("balanced_expert_ids", _vp), ("balanced_active_mask", _vp), ("err_count", _vp),
+        ("expert_ids_stride", _i64), ("eplb_table_stride", _i64), ("expert_scales_stride", _i64),
+        ("threshold_stride", _i64), ("active_mask_stride", _i64), ("out_ids_stride", _i64),
+        ("out_mask_stride", _i64),
     ]

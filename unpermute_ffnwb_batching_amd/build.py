@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libffnwb.so")
+# a measurement probe for the benchmark, in a library of its own (not the product's interface)
+PROBE_SOURCE = "probe_copy.hip"
+PROBE_LIB = os.path.join(LIBDIR, "libffnwb_probe.so")
 SOURCES = ["api.hip", "batching.hip", "unpermute.hip", "permute.hip", "context.hip", "update_expert.hip",
            "noalloc.hip"]
 
@@ -59,16 +62,22 @@ def build(verbose=False):
             print(" ".join(cmd), flush=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs_all = list(ex.map(compile_one, SOURCES + [PROBE_SOURCE]))
+    objs, probe_obj = objs_all[:-1], objs_all[-1]
     tmp = LIB + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    r = subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_LIB + ".tmp", probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print("built", LIB, flush=True)
+        print("built", LIB, "and", PROBE_LIB, flush=True)
     return LIB
 
 

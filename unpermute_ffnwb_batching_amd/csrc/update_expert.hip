@@ -1,6 +1,8 @@
 // MoeUpdateExpert on gfx950 (its README page: "Function description", the parameter
 // table, "Constraints").
 //
+// Every tensor may be strided (the parameter table allows non-contiguous tensors): a row
+// stride per 2-D tensor, an element stride for the threshold and the active mask.
 // At most BS * K = 512 * 16 = 8192 slots: one 1024-thread workgroup takes all of them,
 // 8 per thread.  Its cost is three dependent load rounds (ids and scales; the table
 // counts; the chosen instance ids), so every thread issues each round for all its slots
@@ -18,6 +20,8 @@ constexpr int kUeMaxBs = 512, kUeMaxK = 16, kUeMaxExperts = 1024, kUeMaxWorld = 
 struct UeArgs {
   int32_t n, K, E, F;          // n = BS * K
   int32_t rank, mode;
+  // strides in elements: rows of ids / table / scales / outputs, entries of thr / active
+  int64_t ids_s, tab_s, sc_s, thr_s, act_s, oid_s, om_s;
   const void* ids;
   const int32_t* table;
   const void* scales;
@@ -48,11 +52,12 @@ __global__ __launch_bounds__(kUeThreads) void update_expert_kernel(UeArgs a) {
 #pragma unroll
   for (int r = 0; r < kUePerThread; ++r) {
     const int32_t ic = min(static_cast<int32_t>(threadIdx.x) + r * kUeThreads, a.n - 1);
-    v[r] = static_cast<int64_t>(ids[ic]);
+    const int64_t t = ic / a.K, k = ic - t * a.K;
+    v[r] = static_cast<int64_t>(ids[t * a.ids_s + k]);
     if constexpr (kScales) {
-      sc[r] = load_scale_elem<S>(a.scales, ic);
-      th[r] = a.thr[ic % a.K];
-      act[r] = kActive ? a.active[ic / a.K] : 1;
+      sc[r] = load_scale_elem<S>(a.scales, static_cast<int32_t>(t * a.sc_s + k));
+      th[r] = a.thr[k * a.thr_s];
+      act[r] = kActive ? a.active[t * a.act_s] : 1;
     }
   }
   // round 2: the expert's replica count (row 0 stands in for an id out of range)
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kUeThreads) void update_expert_kernel(UeArgs a) {
 #pragma unroll
   for (int r = 0; r < kUePerThread; ++r) {
     row[r] = (v[r] >= 0 && v[r] < a.E) ? static_cast<int32_t>(v[r]) : 0;
-    cnt[r] = a.table[static_cast<int64_t>(row[r]) * a.F];
+    cnt[r] = a.table[static_cast<int64_t>(row[r]) * a.tab_s];
   }
   // round 3: the chosen replica's instance id
   int32_t inst[kUePerThread];
@@ -71,15 +76,16 @@ __global__ __launch_bounds__(kUeThreads) void update_expert_kernel(UeArgs a) {
     ok[r] = v[r] >= 0 && v[r] < a.E && cnt[r] >= 1 && cnt[r] <= a.F - 1;
     const int32_t c = ok[r] ? cnt[r] : 1;
     const int32_t pick = (a.mode == 0 ? a.rank : i / a.K) % c;   // < c <= F - 1
-    inst[r] = a.table[static_cast<int64_t>(row[r]) * a.F + 1 + pick];
+    inst[r] = a.table[static_cast<int64_t>(row[r]) * a.tab_s + 1 + pick];
   }
   uint32_t nerr = 0;
 #pragma unroll
   for (int r = 0; r < kUePerThread; ++r) {
     const int32_t i = threadIdx.x + r * kUeThreads;
     if (i >= a.n) continue;
-    static_cast<IdT*>(a.out_ids)[i] = static_cast<IdT>(ok[r] ? inst[r] : -1);
-    if constexpr (kScales) a.out_mask[i] = (ok[r] && act[r] != 0 && !(sc[r] < th[r])) ? 1 : 0;
+    const int64_t t = i / a.K, k = i - t * a.K;
+    static_cast<IdT*>(a.out_ids)[t * a.oid_s + k] = static_cast<IdT>(ok[r] ? inst[r] : -1);
+    if constexpr (kScales) a.out_mask[t * a.om_s + k] = (ok[r] && act[r] != 0 && !(sc[r] < th[r])) ? 1 : 0;
     nerr += ok[r] ? 0u : 1u;
   }
   // block sum of the error counts
@@ -117,6 +123,17 @@ int plan_update_expert(const moe_update_expert_desc* d) {
   if (d->balance_mode == 0 && (d->local_rank_id < 0 || d->local_rank_id >= d->world_size))
     return FFNWB_ERR_PARAM_INVALID;
   if (d->table_cols < 2 || d->table_cols > d->world_size + 1) return FFNWB_ERR_PARAM_INVALID;
+  // strides: 0 = dense; a row stride is at least its row, an element stride at least 1;
+  // every element address must fit the kernels' 32-bit scale index (BS * stride < 2^31)
+  const int64_t row_strides[5] = {d->expert_ids_stride, d->expert_scales_stride, d->out_ids_stride,
+                                  d->out_mask_stride, d->eplb_table_stride};
+  for (int i = 0; i < 5; ++i) {
+    const int64_t st = row_strides[i], need = i == 4 ? d->table_cols : d->k;
+    if (st != 0 && (st < need || st > (int64_t{1} << 20))) return FFNWB_ERR_PARAM_INVALID;
+  }
+  if (d->threshold_stride < 0 || d->threshold_stride > (int64_t{1} << 20) || d->active_mask_stride < 0 ||
+      d->active_mask_stride > (int64_t{1} << 20))
+    return FFNWB_ERR_PARAM_INVALID;
   return FFNWB_OK;
 }
 
@@ -151,6 +168,13 @@ int launch_update_expert(const moe_update_expert_desc* d, hipStream_t s) {
   a.out_ids = d->balanced_expert_ids;
   a.out_mask = d->balanced_active_mask;
   a.err_count = d->err_count;
+  a.ids_s = d->expert_ids_stride ? d->expert_ids_stride : d->k;
+  a.tab_s = d->eplb_table_stride ? d->eplb_table_stride : d->table_cols;
+  a.sc_s = d->expert_scales_stride ? d->expert_scales_stride : d->k;
+  a.thr_s = d->threshold_stride ? d->threshold_stride : 1;
+  a.act_s = d->active_mask_stride ? d->active_mask_stride : 1;
+  a.oid_s = d->out_ids_stride ? d->out_ids_stride : d->k;
+  a.om_s = d->out_mask_stride ? d->out_mask_stride : d->k;
   const bool scales = d->expert_scales != nullptr;
   if (d->id_dtype == FFNWB_DT_INT32) launch_ids<int32_t>(a, d->scale_dtype, scales, s);
   else launch_ids<int64_t>(a, d->scale_dtype, scales, s);
