@@ -439,6 +439,12 @@ __global__ __launch_bounds__(256) void batching_copy_kernel(BatchArgs a, const u
   }
 }
 
+// Copy unit of the one-workgroup path: 16, 4 or 1 bytes.
+template <int VEC> struct SmallUnit { typedef u32x4 type; };
+template <> struct SmallUnit<4> { typedef uint32_t type; };
+template <> struct SmallUnit<1> { typedef uint8_t type; };
+constexpr int kSmallUnits = 8;
+
 // All steps in one 256-thread workgroup, for Y <= 1024 slots and <= 4096 keys.
 // LDS: u16 counters [4][nbp] | u32 key starts [nb + 1] | u32 output row of each slot [1024].
 template <int VEC>
@@ -512,21 +518,43 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
     if (err_count != nullptr) *err_count = static_cast<int32_t>(err_w[0] + err_w[1] + err_w[2] + err_w[3]);
   }
   __syncthreads();
+  // each thread places its own slots and writes their row IDs
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t s = static_cast<int64_t>(w) * (kWave * R) + r * kWave + lane;
-    if (s < a.Y) pos_of[s] = val[r] ? start[dig[r]] + hist[w * nbp + dig[r]] + rank[r] : kNoRank;
+    if (s >= a.Y) continue;
+    const uint32_t first = start[dig[r]];
+    const uint32_t pos = first + hist[w * nbp + dig[r]] + rank[r];
+    pos_of[s] = val[r] ? pos : kNoRank;
+    if (val[r]) write_row_ids(a, s, pos, first);
   }
   __syncthreads();
-  for (int64_t s = w; s < a.Y; s += kRankWaves) {
-    const uint32_t pos = pos_of[s];
-    if (pos == kNoRank) continue;
-    if (lane == 0) {
-      bool v, e;
-      const uint32_t key = ks.key(s, v, e);
-      write_row_ids(a, s, pos, start[key]);
+  // the rows as one flat run of VEC-byte units over all threads (Y * row_bytes <= 4 MiB),
+  // kSmallUnits loads in flight per thread: one memory round trip for a small problem
+  // instead of one per row and wavefront
+  typedef typename SmallUnit<VEC>::type U;
+  const uint32_t nu = static_cast<uint32_t>(a.row_bytes / VEC);
+  const uint32_t total = static_cast<uint32_t>(a.Y) * nu;
+  for (uint32_t u0 = threadIdx.x; u0 < total; u0 += kRankThreads * kSmallUnits) {
+    U v[kSmallUnits];
+    uint32_t dst[kSmallUnits];
+#pragma unroll
+    for (int k = 0; k < kSmallUnits; ++k) {
+      const uint32_t u = u0 + k * kRankThreads;
+      const uint32_t sl = min(u, total - 1) / nu;
+      const uint32_t part = min(u, total - 1) - sl * nu;
+      const uint32_t pos = pos_of[sl];
+      const bool placed = u < total && pos != kNoRank;
+      dst[k] = placed ? pos * nu + part : 0xffffffffu;
+      // an unplaced slot's row is never read (from a rejected ScheduleContext its address
+      // is 0): its load takes the output's first unit instead, so every load stays
+      // unconditional and in bounds
+      const U* src = placed ? reinterpret_cast<const U*>(slot_row(a, sl)) + part : reinterpret_cast<const U*>(a.y);
+      v[k] = *src;
     }
-    copy_row<VEC>(slot_row(a, s), a.y + static_cast<int64_t>(pos) * a.row_bytes, a.row_bytes, lane);
+#pragma unroll
+    for (int k = 0; k < kSmallUnits; ++k)
+      if (dst[k] != 0xffffffffu) reinterpret_cast<U*>(a.y)[dst[k]] = v[k];
   }
 }
 
