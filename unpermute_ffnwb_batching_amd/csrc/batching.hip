@@ -563,8 +563,8 @@ __global__ __launch_bounds__(256) void batching_small_kernel(BatchArgs a, int nb
 // tile-major histogram (nt x nb words, in L2) and sums each key's column over all tiles
 // and over the tiles before t.  An exclusive scan of the sums gives each key's first
 // output row, so every workgroup places its own tile's slots without waiting for another:
-// inv[row] = slot.  Workgroup 0 writes every key's first row to kstart, group_list,
-// actual_token_num and err_count.  The row copy that follows walks the output rows
+// inv[row] = slot.  Every workgroup writes the first rows (kstart) and group_list rows
+// of its share of the keys; workgroup 0 writes actual_token_num and err_count.  The row copy that follows walks the output rows
 // (random reads, sequential writes, which measured faster than walking the slots) and
 // writes the row IDs, in row order.
 // LDS: key sums -> first rows [nb] | sums before the tile [nb].
@@ -615,8 +615,11 @@ __global__ __launch_bounds__(kWgThreads) void batching_place_kernel(BatchArgs a,
   }
   __syncthreads();
   // 2. cnt[k] <- first output row of key k (one scan of [sums | presence]: the presence
-  //    prefix is offset by the sums' total); workgroup 0 writes kstart and group_list
+  //    prefix is offset by the sums' total).  Every workgroup holds the whole scan, so
+  //    each writes the key starts and group_list rows of its own share of the keys
   const bool g0 = t == 0;
+  const int share = (nb + nt - 1) / nt;
+  const int klo = t * share, khi = min(nb, klo + share);
   uint32_t carry = 0, gcarry = 0;
   for (int k0 = 0, it = 0; k0 < nb; k0 += kWgThreads, it ^= 1) {
     const int kk = k0 + threadIdx.x;
@@ -625,9 +628,10 @@ __global__ __launch_bounds__(kWgThreads) void batching_place_kernel(BatchArgs a,
     uint32_t all;
     block_exscan_multi<kWgThreads, 2>(v, wsum[it], all);
     const uint32_t tot = wsum[it][kWgWaves];  // sequence 1 starts after all sums
+    const bool mine = kk >= klo && kk < khi;
     if (kk < nb) cnt[kk] = carry + v[0];
-    if (g0 && kk < nb) kstart[kk] = carry + v[0];
-    if (g0 && c > 0) {
+    if (mine) kstart[kk] = carry + v[0];
+    if (mine && c > 0) {
       const int64_t slot = gcarry + v[1] - tot;
       group_list[2 * slot] = kk;
       group_list[2 * slot + 1] = c;
@@ -635,11 +639,17 @@ __global__ __launch_bounds__(kWgThreads) void batching_place_kernel(BatchArgs a,
     carry += tot;
     gcarry += all - tot;
   }
-  if (g0) {
-    for (int64_t g = gcarry + threadIdx.x; g < group_rows; g += kWgThreads) {
+  // the {0, 0} rows after the present keys, split over the workgroups
+  {
+    const int64_t zrows = group_rows - gcarry;
+    const int64_t zshare = (zrows + nt - 1) / nt;
+    const int64_t zlo = gcarry + t * zshare, zhi = min(group_rows, zlo + zshare);
+    for (int64_t g = zlo + threadIdx.x; g < zhi; g += kWgThreads) {
       group_list[2 * g] = 0;
       group_list[2 * g + 1] = 0;
     }
+  }
+  if (g0) {
     uint32_t e = 0;
     for (int u = threadIdx.x; u < nt; u += kWgThreads) e += tile_err[u];
     e = wave_sum(e);
@@ -947,8 +957,15 @@ int launch_batching(const ffnwb_batching_desc* d, const BatchingPlan& p, void* w
                          static_cast<const uint32_t*>(tile_err), nb, p.pass.nt, p.pass.tile_shift, inv, kstart,
                          d->group_list, d->expert_num, d->actual_token_num, d->err_count);
     };
-    if (p.pass.nt <= 16) place(std::integral_constant<int, 16>());
-    else if (p.pass.nt <= 32) place(std::integral_constant<int, 32>());
+    // as many histogram loads in flight as there are tiles (clamped duplicates cost
+    // L2-to-CU bandwidth: 64 loads for 36 tiles measured 9-11 us, 40 loads 7.3 us)
+    const int nt = p.pass.nt;
+    if (nt <= 8) place(std::integral_constant<int, 8>());
+    else if (nt <= 16) place(std::integral_constant<int, 16>());
+    else if (nt <= 24) place(std::integral_constant<int, 24>());
+    else if (nt <= 32) place(std::integral_constant<int, 32>());
+    else if (nt <= 40) place(std::integral_constant<int, 40>());
+    else if (nt <= 48) place(std::integral_constant<int, 48>());
     else place(std::integral_constant<int, 64>());
     if ((err = hipGetLastError()) != hipSuccess) return FFNWB_ERR_RUNTIME;
     const unsigned blocks = static_cast<unsigned>((p.Y + 3) / 4);
