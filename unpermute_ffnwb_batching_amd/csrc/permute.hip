@@ -388,21 +388,26 @@ __device__ __forceinline__ void zero_row(uint8_t* __restrict__ dst, int64_t row_
   }
 }
 
-// Row moves.  Workgroups below token_blocks: one wavefront per token reads its list
-// (lists[t*K .. t*K+K), -1 = none; K = topK non-padded, E padded or from the [T][E]
-// table) 64 entries at a time and gathers the rows in [0, N) it names into a per-wave LDS
-// list; then it loads each 16 KiB piece of the token's row once and stores it to every
-// listed row, with ordinary stores: this kernel writes several times what it reads, and
-// for such write-heavy traffic ordinary stores measured 4% faster than non-temporal ones
-// (242 vs 251 us at T=16384, topK=8, H=4096 BF16).  With topk > 0 the list is the
-// non-padded table, and the wavefront also writes the token's slots: sorted_out[t*topk +
-// k] = the row of its k-th listed entry (-1 past N, and for k past its entries).
+// Row moves.  Workgroups below token_blocks: S wavefronts per token (consecutive global
+// wavefront numbers) read its list (lists[t*K .. t*K+K), -1 = none; K = topK non-padded,
+// E padded or from the [T][E] table) 64 entries at a time; wavefront `sub` gathers the
+// listed rows in [0, N) whose list index is sub (mod S) into a per-wave LDS list, then
+// loads each 16 KiB piece of the token's row once and stores it to every row of its
+// list, with ordinary stores: this kernel writes several times what it reads, and for
+// such write-heavy traffic ordinary stores measured faster than non-temporal ones (243
+// vs 250 us at T=16384, topK=8, H=4096 BF16).  Non-padded, 4 wavefronts per token with
+// ordinary loads (the token's row is read from HBM once and from L2 by the others)
+// measured 225 us against 243 us for one; padded (4 rows per token, 10 KiB each) one
+// wavefront with non-temporal loads stays fastest (86 against 91 us).  With topk > 0
+// the list is the non-padded table, and wavefront 0 of the token also writes its
+// slots: sorted_out[t*topk + k] = the row of its k-th listed entry (-1 past N, and for k
+// past its entries).
 // The rest: one wavefront per 64 output rows handles the rows no list names:
 // source_of[r] = -1 (zeros) or -(t+2) (token t), or, without source_of, zeros for the
 // rows from *filled (the number of non-zero entries) up to N.
 constexpr int kDestCap = 256;  // listed rows a wavefront gathers before it copies
 
-template <int VEC>
+template <int VEC, bool CACHED>
 __device__ __forceinline__ void copy_to_rows(const uint8_t* __restrict__ src, int64_t row_bytes,
                                              const int32_t* rows, uint32_t nd, uint8_t* __restrict__ out,
                                              uint32_t lane) {
@@ -413,7 +418,8 @@ __device__ __forceinline__ void copy_to_rows(const uint8_t* __restrict__ src, in
   const int64_t n16 = row_bytes >> 4;
   for (int64_t b = 0; b < n16; b += kWave * kPiece) {
     RowPiece<VEC> piece;
-    piece.load(src, n16, b, lane);
+    if (CACHED) piece.load_cached(src, n16, b, lane);
+    else piece.load(src, n16, b, lane);
     for (uint32_t j = 0; j < nd; ++j) piece.store_cached(out + static_cast<int64_t>(rows[j]) * row_bytes, n16, b, lane);
   }
   if (VEC == 4) {
@@ -425,7 +431,7 @@ __device__ __forceinline__ void copy_to_rows(const uint8_t* __restrict__ src, in
   }
 }
 
-template <int VEC>
+template <int VEC, int S, bool CACHED>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __restrict__ tokens, int64_t stride,
                                                               int64_t row_bytes,
                                                               const int32_t* __restrict__ lists, int64_t T,
@@ -433,12 +439,14 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __r
                                                               int32_t* __restrict__ sorted_out,
                                                               const int32_t* __restrict__ source_of,
                                                               const uint32_t* __restrict__ filled, int64_t N,
-                                                              unsigned token_blocks, uint8_t* __restrict__ out) {
+                                                              uint8_t* __restrict__ out, unsigned token_blocks) {
   __shared__ int32_t dests[4][kDestCap];
   const uint32_t lane = lane_id();
   const int wv = uniform(static_cast<int>(threadIdx.x) / kWave);
   if (blockIdx.x < token_blocks) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+    const int64_t t = gw / S;
+    const int sub = static_cast<int>(gw % S);
     if (t >= T) return;
     const uint8_t* src = tokens + t * stride;
     int32_t* dl = dests[wv];
@@ -448,26 +456,26 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint8_t* __r
       if (topk > 0) {
         const uint64_t nz = wave_ballot(d != -1);
         const uint32_t k = k0 + count_below(nz);
-        if (d != -1 && k < static_cast<uint32_t>(topk))
+        if (sub == 0 && d != -1 && k < static_cast<uint32_t>(topk))
           sorted_out[t * topk + k] = (d >= 0 && d < N) ? d : -1;
         k0 += static_cast<uint32_t>(__popcll(nz));
       }
-      const bool ok = d >= 0 && d < N;
+      const bool ok = d >= 0 && d < N && (S == 1 || (c0 + static_cast<int>(lane)) % S == sub);
       const uint64_t m = wave_ballot(ok);
       if (ok) dl[nd + count_below(m)] = d;
       nd += static_cast<uint32_t>(__popcll(m));
       if (nd > kDestCap - kWave) {  // the next chunk might not fit: copy now
         wave_lds_sync();
-        copy_to_rows<VEC>(src, row_bytes, dl, nd, out, lane);
+        copy_to_rows<VEC, CACHED>(src, row_bytes, dl, nd, out, lane);
         wave_lds_sync();
         nd = 0;
       }
     }
-    if (topk > 0)
+    if (topk > 0 && sub == 0)
       for (uint32_t q = k0 + lane; q < static_cast<uint32_t>(topk); q += kWave) sorted_out[t * topk + q] = -1;
     if (nd > 0) {
       wave_lds_sync();
-      copy_to_rows<VEC>(src, row_bytes, dl, nd, out, lane);
+      copy_to_rows<VEC, CACHED>(src, row_bytes, dl, nd, out, lane);
     }
     return;
   }
@@ -543,11 +551,16 @@ int plan_permute(const moe_permute_desc* d, PermutePlan* p) {
   return FFNWB_OK;
 }
 
-template <typename... Args>
-static bool launch_scatter(int vec, dim3 grid, hipStream_t s, void* evb, void* eve, Args... args) {
-  if (vec == 16) return launch_bound(permute_scatter_kernel<16>, grid, dim3(256), 0, s, evb, eve, args...);
-  if (vec == 4) return launch_bound(permute_scatter_kernel<4>, grid, dim3(256), 0, s, evb, eve, args...);
-  return launch_bound(permute_scatter_kernel<1>, grid, dim3(256), 0, s, evb, eve, args...);
+// S wavefronts per token (4 with ordinary loads for the non-padded slot lists, else 1
+// with non-temporal loads); the row pass follows the token blocks.
+template <int S, bool CACHED, typename... Args>
+static bool launch_scatter(int vec, int64_t T, int64_t N, hipStream_t s, void* evb, void* eve, Args... args) {
+  const unsigned tb = static_cast<unsigned>((T * S + 3) / 4);
+  const unsigned rb = static_cast<unsigned>((N + 4 * kWave - 1) / (4 * kWave));
+  const dim3 grid(tb + rb);
+  if (vec == 16) return launch_bound(permute_scatter_kernel<16, S, CACHED>, grid, dim3(256), 0, s, evb, eve, args..., tb);
+  if (vec == 4) return launch_bound(permute_scatter_kernel<4, S, CACHED>, grid, dim3(256), 0, s, evb, eve, args..., tb);
+  return launch_bound(permute_scatter_kernel<1, S, CACHED>, grid, dim3(256), 0, s, evb, eve, args..., tb);
 }
 
 int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hipStream_t s) {
@@ -563,8 +576,6 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   // the optional hooks are bound to the row-copy launch
   void* evb = d->ev_copy_begin;
   void* eve = d->ev_copy_end;
-  const unsigned tb = static_cast<unsigned>((p.T + 3) / 4);
-  const unsigned rb = static_cast<unsigned>((p.N + 4 * kWave - 1) / (4 * kWave));
   if (p.table) {
     const int nt32 = static_cast<int>((p.T + kMaskTile - 1) / kMaskTile);
     uint32_t* hist = c.take<uint32_t>(static_cast<size_t>(nt32) * E);
@@ -587,11 +598,11 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
     if (hipGetLastError() != hipSuccess) return FFNWB_ERR_RUNTIME;
     // padded: rows whose sorted_indices entry is -1 are zero; non-padded: rows from the
     // number of non-zero entries (start[E]) on
-    const bool ok = launch_scatter(vec, dim3(tb + rb), s, evb, eve, tok, p.stride, p.row_bytes,
+    const bool ok = launch_scatter<1, false>(vec, p.T, p.N, s, evb, eve, tok, p.stride, p.row_bytes,
                                    static_cast<const int32_t*>(table), p.T, E,
                                    static_cast<int32_t>(p.padded ? 0 : p.K), d->sorted_indices,
                                    static_cast<const int32_t*>(p.padded ? d->sorted_indices : nullptr),
-                                   static_cast<const uint32_t*>(start + E), p.N, tb, out);
+                                   static_cast<const uint32_t*>(start + E), p.N, out);
     if (!ok) return FFNWB_ERR_RUNTIME;
     return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
   }
@@ -622,9 +633,14 @@ int launch_permute(const moe_permute_desc* d, const PermutePlan& p, void* ws, hi
   // source_of), padded through the [T][E] table (zero rows are sorted_indices' -1 entries)
   const int32_t K = static_cast<int32_t>(p.padded ? p.E : p.K);
   const int32_t* lists = p.padded ? dest : d->sorted_indices;
-  const bool ok = launch_scatter(vec, dim3(tb + rb), s, evb, eve, tok, p.stride, p.row_bytes, lists, p.T, K,
-                                 int32_t{0}, static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(source_of),
-                                 static_cast<const uint32_t*>(nullptr), p.N, tb, out);
+  const int32_t* src_of = source_of;
+  int32_t* no_slots = nullptr;
+  const uint32_t* no_filled = nullptr;
+  const bool ok =
+      p.padded ? launch_scatter<1, false>(vec, p.T, p.N, s, evb, eve, tok, p.stride, p.row_bytes, lists, p.T, K,
+                                          int32_t{0}, no_slots, src_of, no_filled, p.N, out)
+               : launch_scatter<4, true>(vec, p.T, p.N, s, evb, eve, tok, p.stride, p.row_bytes, lists, p.T, K,
+                                         int32_t{0}, no_slots, src_of, no_filled, p.N, out);
   if (!ok) return FFNWB_ERR_RUNTIME;
   return hipGetLastError() == hipSuccess ? FFNWB_OK : FFNWB_ERR_RUNTIME;
 }

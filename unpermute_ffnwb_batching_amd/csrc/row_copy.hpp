@@ -26,6 +26,17 @@ struct RowPiece {
       if (i < n16) v[u] = __builtin_nontemporal_load(s4 + i);  // streamed once: do not keep in cache
     }
   }
+  // the same with ordinary loads, for a row several wavefronts read at once (the later
+  // reads hit in L2)
+  __device__ __forceinline__ void load_cached(const uint8_t* __restrict__ src, int64_t n16, int64_t b,
+                                              uint32_t lane) {
+    const V* s4 = reinterpret_cast<const V*>(src);
+#pragma unroll
+    for (int u = 0; u < kPiece; ++u) {
+      const int64_t i = b + u * kWave + lane;
+      if (i < n16) v[u] = s4[i];
+    }
+  }
   __device__ __forceinline__ void store(uint8_t* __restrict__ dst, int64_t n16, int64_t b, uint32_t lane) const {
     V* d4 = reinterpret_cast<V*>(dst);
 #pragma unroll
