@@ -11,8 +11,8 @@
 //   [aux]    out_index / permute_token_id: stable sort of the slots by sortedIndices+1
 //            (LSD passes when the row count exceeds one pass's bucket budget), on the
 //            caller's stream, or on the caller's auxiliary stream when the descriptor
-//            names one: forked when the compaction's first kernel completes and joined
-//            after the reduce.
+//            names one: forked when the compaction's first kernel completes, submitted
+//            after the reduce and joined after it.
 // Padded mode (branches 1 and 3):
 //   invert:  stable counting sort of the capacity entries by token id (rank, scan,
 //            scatter -> out_index, permute_token_id, permute_probs, per-token segments);
@@ -679,7 +679,11 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
                       reinterpret_cast<uintptr_t>(d->probs) % (4 * p.pelt) == 0;
     // 1. the first kernel on the caller's stream: the compaction's count kernel, whose
     //    completion (all earlier work on the stream done) is the fork point; without it a
-    //    fork event is recorded
+    //    fork event is recorded.  The auxiliary order is submitted after the reduce (it
+    //    reads only sortedIndices and writes only its own outputs and workspace): on an
+    //    idle GPU the caller's kernels are dispatched first, and the auxiliary stream's
+    //    wait usually finds its fork point already passed (an isolated call 260 -> 228 us
+    //    on the non-padded workload).
     bool forked = false;
     if (fused) {
       void* fork_ev = side != nullptr ? static_cast<void*>(side->fork) : nullptr;
@@ -693,27 +697,6 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
       forked = fork_ev != nullptr;
     } else if (side != nullptr) {
       forked = hipEventRecord(side->fork, s) == hipSuccess;
-    }
-    if (aux) {
-      hipStream_t as = s;
-      if (side != nullptr) {
-        if (!forked || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
-        as = side->stream;
-      }
-      KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
-      const uint32_t *kin, *vin;
-      const Placement pl = run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, as);
-      const unsigned g = grid_for(p.N, 256);
-      if (p.sort.npasses == 1)
-        hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, as, ks,
-                           static_cast<const uint32_t*>(nullptr), pl, p.N, static_cast<uint32_t*>(nullptr),
-                           static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
-                           static_cast<int32_t>(p.K));
-      else
-        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, as, KeyArray{kin}, vin,
-                           pl, p.N, static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
-                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
-      if (side != nullptr && hipEventRecord(side->join, side->stream) != hipSuccess) return FFNWB_ERR_RUNTIME;
     }
     // 2. the rest of the probs compaction, then the gather-reduce, on the caller's stream
     if (fused) {
@@ -751,6 +734,28 @@ int launch_unpermute(const moe_unpermute_desc* d, const UnpermutePlan& p, void* 
     const int mode = !p.has_probs ? kNonPad : (d->weight_index == 1 ? kNonPadW1 : kNonPadW2);
     if (!launch_reduce(ra, d->dtype, d->probs_dtype, mode, shape, p.T, s, d->ev_reduce_begin, d->ev_reduce_end))
       return FFNWB_ERR_RUNTIME;
+    // 3. the auxiliary order, then the join
+    if (aux) {
+      hipStream_t as = s;
+      if (side != nullptr) {
+        if (!forked || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
+        as = side->stream;
+      }
+      KeyNonPadded ks{sI, static_cast<int32_t>(p.rows)};
+      const uint32_t *kin, *vin;
+      const Placement pl = run_passes_but_last_scatter(p.sort, ks, b, &kin, &vin, as);
+      const unsigned g = grid_for(p.N, 256);
+      if (p.sort.npasses == 1)
+        hipLaunchKernelGGL((lsd_scatter_kernel<KeyNonPadded, true, 1>), dim3(g), dim3(256), 0, as, ks,
+                           static_cast<const uint32_t*>(nullptr), pl, p.N, static_cast<uint32_t*>(nullptr),
+                           static_cast<uint32_t*>(nullptr), d->out_index, d->permute_token_id, sI,
+                           static_cast<int32_t>(p.K));
+      else
+        hipLaunchKernelGGL((lsd_scatter_kernel<KeyArray, false, 1>), dim3(g), dim3(256), 0, as, KeyArray{kin}, vin,
+                           pl, p.N, static_cast<uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr), d->out_index,
+                           d->permute_token_id, sI, static_cast<int32_t>(p.K));
+      if (side != nullptr && hipEventRecord(side->join, side->stream) != hipSuccess) return FFNWB_ERR_RUNTIME;
+    }
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return FFNWB_ERR_RUNTIME;
   } else {
     SortBufs b{};
